@@ -1,0 +1,52 @@
+"""Comparison rules between a device result and the fp64 oracle.
+
+official:  max |gpu - ref| <= 1e-2 * (1 + |ref|)            (elementwise)
+strict:    |gpu - ref| <= 1e-2 * (rms(ref) + |ref|)          (elementwise)
+           and ||gpu - ref||_2 / ||ref||_2 <= 2^-7
+The official bound alone has an absolute floor of 1e-2, far above the
+typical magnitude of these outputs (an all-zero answer would pass), so
+every parity test applies both.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NRMSE_MAX = 2.0 ** -7
+
+
+def _f64(a) -> np.ndarray:
+    try:
+        import torch
+
+        if isinstance(a, torch.Tensor):
+            return a.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
+
+
+def errors(gpu, ref) -> dict:
+    g, r = _f64(gpu), _f64(ref)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    err = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    return {
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "official_ratio": float((err / (1.0 + np.abs(r))).max()) / 1e-2 if err.size else 0.0,
+        "strict_ratio": float((err / (rms + np.abs(r) + 1e-300)).max()) / 1e-2 if err.size else 0.0,
+        "nrmse": float(np.sqrt(np.mean(err * err)) / rms) if rms > 0 else float(err.max() if err.size else 0.0),
+        "rms_ref": rms,
+        "finite": bool(np.isfinite(g).all()),
+    }
+
+
+def passes(gpu, ref) -> bool:
+    e = errors(gpu, ref)
+    return e["finite"] and e["official_ratio"] <= 1.0 and e["strict_ratio"] <= 1.0 and e["nrmse"] <= NRMSE_MAX
+
+
+def assert_parity(gpu, ref, name: str = "") -> dict:
+    e = errors(gpu, ref)
+    ok = e["finite"] and e["official_ratio"] <= 1.0 and e["strict_ratio"] <= 1.0 and e["nrmse"] <= NRMSE_MAX
+    assert ok, f"{name}: parity failed {e}"
+    return e
