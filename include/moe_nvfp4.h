@@ -1,0 +1,203 @@
+/*
+ * moe_nvfp4.h — C ABI of the grouped NVFP4 mixture-of-experts expert
+ * projection for AMD Instinct MI355X (gfx950).
+ *
+ * The path has four calls per MoE layer, issued in this order on one stream:
+ *
+ *   moe_nvfp4_sort          group the routed (token, expert) pairs by expert
+ *   moe_nvfp4_gate_up_silu  h = silu(x Wg^T) * (x Wu^T) per routed pair
+ *   moe_nvfp4_down          y = h Wd^T per routed pair
+ *   moe_nvfp4_blend         out[t] = sum_j w[t, j] * y[pair of (t, j)]
+ *
+ * plus a load-time byte transpose, transpose_u8, that builds the K-major
+ * "transposed twin" of a weight for the many-token path.
+ *
+ * Sources of the operations (the reference pages are Rust source pages of a
+ * model runtime; each is cited by its file name and the item on it):
+ *   - NVFP4 layout: quant_shard.rs, layout comment above shard_quantized_nvfp4
+ *     (packed [N, K/2] u8 E2M1 nibbles, [N, K/group] u8 E4M3 scales, one f32
+ *     per-tensor scale_2); nvfp4_moe_grouped.rs, module doc (group 16).
+ *   - Sort, gate+up+SiLU, down, blend: nvfp4_moe_grouped.rs, module doc and
+ *     the docs of moe_expert_gate_up_act_nvfp4_grouped and
+ *     moe_expert_down_act_nvfp4_grouped; the per-expert pointer tables are
+ *     that page's Nvfp4ExpertTables.
+ *   - Transposed twin: transpose.rs, transpose_for_gemm / transpose_for_gemm_gs
+ *     (packed [N, K/2] -> [K/2, N], scales [N, K/16] -> [K/16, N]).
+ *   - NULL experts contribute nothing: expert.rs, ExpertWeight::null.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *     caller owns every buffer.  The library allocates nothing, frees nothing,
+ *     keeps no state between calls and never synchronizes: each call only
+ *     enqueues work on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Outputs never alias inputs.
+ *   - Return value: MOE_NVFP4_OK (0) on success; a negative MOE_NVFP4_E*
+ *     code when the host-side argument check fails, in which case NOTHING
+ *     was launched; a positive hipError_t if a launch itself failed.
+ *   - Shapes: T tokens, k experts per token (top-k), P = T * k routed pairs,
+ *     E experts, H hidden width, I expert intermediate width.  Matrices are
+ *     row-major and dense (row stride = row length).
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_NVFP4_ABI_VERSION 1
+
+/* Weight layouts of a projection [N, K] (N outputs, K inputs). */
+#define MOE_NVFP4_ROW_MAJOR 0 /* packed [N, K/2], scales [N, K/16]  (decode GEMV path) */
+#define MOE_NVFP4_K_MAJOR   1 /* packed [K/2, N], scales [K/16, N]  (many-token MFMA path) */
+
+/* Host-side argument errors (nothing is launched). */
+#define MOE_NVFP4_OK          0
+#define MOE_NVFP4_ENULL      -1 /* a required pointer is NULL                          */
+#define MOE_NVFP4_ESHAPE     -2 /* a size is out of range or not admitted (see call)    */
+#define MOE_NVFP4_ELAYOUT    -3 /* unknown layout, or gate/up layouts differ            */
+#define MOE_NVFP4_ELIMIT     -4 /* a size exceeds a documented maximum of the call      */
+
+/* Device error flag bits (moe_nvfp4_sort's err_flag). */
+#define MOE_NVFP4_FLAG_BAD_EXPERT_ID 1u
+
+/*
+ * One NVFP4 projection across the experts (the pages' Nvfp4ExpertTables):
+ * device arrays of E device pointers and E floats.
+ *   packed[e]  E2M1 nibbles, two per byte, low nibble = even k.
+ *              ROW_MAJOR: [N, K/2]; K_MAJOR: [K/2, N].
+ *   scale[e]   E4M3 (OCP "FN": bias 7, max 448, NaN = S.1111.111) block
+ *              scales, one per 16 consecutive k.  ROW_MAJOR: [N, K/16];
+ *              K_MAJOR: [K/16, N].
+ *   scale2[e]  the per-tensor f32 scale_2.
+ * Weight element (n, k) = e2m1(nibble) * e4m3(scale of group k/16) * scale_2.
+ * packed[e] == NULL marks an absent expert (not owned under expert
+ * parallelism): its rows of h and y are written as 0, so it contributes 0.
+ * Scale codes must not be NaN (0x7F, 0xFF): results are then unspecified.
+ */
+typedef struct {
+    const uint8_t *const *packed;
+    const uint8_t *const *scale;
+    const float *scale2;
+    int32_t layout; /* MOE_NVFP4_ROW_MAJOR or MOE_NVFP4_K_MAJOR */
+} moe_nvfp4_experts;
+
+/* Maximum sizes admitted by the calls below. */
+#define MOE_NVFP4_MAX_EXPERTS 1024
+#define MOE_NVFP4_MAX_PAIRS   (1 << 22)
+#define MOE_NVFP4_MAX_WIDTH   (1 << 16) /* H and I */
+
+/*
+ * moe_nvfp4_sort — group the P = T*k routed pairs by expert
+ * (nvfp4_moe_grouped.rs, module doc: rows grouped by expert, active experts
+ * listed, intermediates laid out by sorted position).
+ *
+ *   topk_ids          in  int32 [T, k]  expert of pair f = t*k + j.
+ *   expert_offsets    out int32 [E+1]   exclusive prefix sum of the per-expert
+ *                                       pair counts; rows of expert e are the
+ *                                       sorted positions [off[e], off[e+1]).
+ *   sorted_token_ids  out int32 [P]     token t of the pair at each sorted
+ *                                       position; -1 past the last valid pair.
+ *   pair_pos          out int32 [P]     sorted position of flat pair f; -1 for
+ *                                       a pair with an invalid expert id.
+ *   active_experts    out int32 [E]     experts with at least one pair, in
+ *                                       ascending id order; -1 past the count.
+ *   active_count      out int32 [1]     number of active experts.
+ *   err_flag          in/out uint32 [1] zeroed by the caller; OR-ed with
+ *                                       MOE_NVFP4_FLAG_BAD_EXPERT_ID if any id
+ *                                       lies outside [0, E).  Such a pair joins
+ *                                       no expert and contributes 0.
+ * Order within an expert is by flat pair index (stable), so every output is
+ * unique and deterministic.  Errors: ENULL; ESHAPE if T < 1, k < 1, E < 1 or
+ * k > E; ELIMIT if E > MOE_NVFP4_MAX_EXPERTS or P > MOE_NVFP4_MAX_PAIRS.
+ */
+int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                   int32_t *expert_offsets, int32_t *sorted_token_ids, int32_t *pair_pos,
+                   int32_t *active_experts, int32_t *active_count, uint32_t *err_flag,
+                   void *stream);
+
+/*
+ * moe_nvfp4_gate_up_silu — fused gate+up projection and SiLU product
+ * (nvfp4_moe_grouped.rs, doc of moe_expert_gate_up_act_nvfp4_grouped).
+ * For every active expert e and every sorted position p of e, with token
+ * t = sorted_token_ids[p] and n < I:
+ *     g = sum_k x[t, k] * Wg_e[n, k],   u = sum_k x[t, k] * Wu_e[n, k],
+ *     h[p, n] = g / (1 + exp(-g)) * u        (fp32 accumulation and output)
+ *
+ *   x                 in  bf16 [T, H]
+ *   gate, up          NVFP4 tables, N = I, K = H, both in the same layout.
+ *                     ROW_MAJOR runs the decode GEMV (few tokens per expert);
+ *                     K_MAJOR runs the grouped MFMA GEMM (many tokens).
+ *   expert_offsets, sorted_token_ids, active_experts, active_count:
+ *                     moe_nvfp4_sort's outputs (read on the device only).
+ *   h                 out fp32 [P, I]; rows of positions that belong to no
+ *                     active expert are left untouched.
+ * Admission: H % 32 == 0 and I % 32 == 0 (ROW_MAJOR); H % 64 == 0 and
+ * I % 64 == 0 (K_MAJOR).  The K_MAJOR path feeds the matrix cores with fp16
+ * operands, so it admits activations of magnitude below 65504.
+ * Errors: ENULL, ESHAPE, ELAYOUT, ELIMIT (E, P or width above the maxima).
+ */
+int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
+                           int32_t I, moe_nvfp4_experts gate, moe_nvfp4_experts up,
+                           const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                           const int32_t *active_experts, const int32_t *active_count,
+                           float *h, void *stream);
+
+/*
+ * moe_nvfp4_down — down projection over the SiLU product
+ * (nvfp4_moe_grouped.rs, doc of moe_expert_down_act_nvfp4_grouped: k is the
+ * intermediate width, rows of the activation and output are sorted
+ * positions).  For every active expert e, position p of e and n < H:
+ *     y[p, n] = sum_i h[p, i] * Wd_e[n, i]          (fp32 accumulation)
+ *
+ *   h      in  fp32 [P, I]   (the kernels round it to 16-bit floats for
+ *                             the products; accumulation stays fp32)
+ *   down   NVFP4 table, N = H, K = I.
+ *   y      out fp32 [P, H]; rows of positions outside every active expert are
+ *          left untouched.
+ * Admission and errors as moe_nvfp4_gate_up_silu.
+ */
+int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                   moe_nvfp4_experts down, const int32_t *expert_offsets,
+                   const int32_t *active_experts, const int32_t *active_count, float *y,
+                   void *stream);
+
+/*
+ * moe_nvfp4_blend — weighted sum of each token's top-k outputs
+ * (nvfp4_moe_grouped.rs, module doc: the weighted-sum blend).
+ *     out[t, n] = bf16_rne( sum_{j=0..k-1} topk_weights[t, j] * y[pair_pos[t*k+j], n] )
+ * summed in fp32 in ascending j; a pair with pair_pos < 0 adds nothing.
+ *
+ *   y             in  fp32 [P, H]
+ *   topk_weights  in  fp32 [T, k]
+ *   pair_pos      in  int32 [T*k]  (moe_nvfp4_sort's output)
+ *   out           out bf16 [T, H]
+ * Errors: ENULL; ESHAPE if T < 1, k < 1 or H < 1; ELIMIT if P or H exceed
+ * the maxima.
+ */
+int moe_nvfp4_blend(const float *y, const float *topk_weights, const int32_t *pair_pos,
+                    int32_t T, int32_t k, int32_t H, uint16_t *out, void *stream);
+
+/*
+ * transpose_u8 — out-of-place byte-matrix transpose
+ * (transpose.rs, transpose_for_gemm_gs and its host loop):
+ *     dst[c * rows + r] = src[r * cols + c]     for r < rows, c < cols.
+ * Applied to a packed weight with rows = N, cols = K/2 and to its scales
+ * with rows = N, cols = K/16, it builds the K_MAJOR twin.  src is left
+ * unchanged; src and dst must not overlap.
+ * Errors: ENULL; ESHAPE if rows < 1 or cols < 1; ELIMIT if rows * cols
+ * exceeds 2^40 bytes.
+ */
+int transpose_u8(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, void *stream);
+
+/* ABI version of the loaded library (MOE_NVFP4_ABI_VERSION). */
+int moe_nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

@@ -1,0 +1,263 @@
+"""Grouped NVFP4 MoE expert projection for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/moe_nvfp4.h``: the five
+entry points keep their C names and take torch tensors only for device
+memory and streams; every step of the path runs in the HIP kernels of
+``libmoe_nvfp4.so``.  There is no CPU fallback: importing works without the
+library, but the first call raises if it is missing.
+
+Higher-level helpers:
+  * ``ExpertTables``       device pointer tables of one projection across experts
+                           (nvfp4_moe_grouped.rs, ``Nvfp4ExpertTables``);
+  * ``transpose_for_gemm`` load-time K-major twin of one NVFP4 weight
+                           (transpose.rs, ``transpose_for_gemm``);
+  * ``MoeLayer``           the four calls of one layer forward on one stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "ExpertTables",
+    "MoeLayer",
+    "MoeNvfp4Error",
+    "ROW_MAJOR",
+    "K_MAJOR",
+    "FLAG_BAD_EXPERT_ID",
+    "lib",
+    "header_functions",
+    "moe_nvfp4_sort",
+    "moe_nvfp4_gate_up_silu",
+    "moe_nvfp4_down",
+    "moe_nvfp4_blend",
+    "transpose_u8",
+    "transpose_for_gemm",
+]
+
+ROW_MAJOR = 0
+K_MAJOR = 1
+FLAG_BAD_EXPERT_ID = 1
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libmoe_nvfp4.so"
+HEADER = _PKG.parent / "include" / "moe_nvfp4.h"
+
+_ERRNAMES = {-1: "ENULL", -2: "ESHAPE", -3: "ELAYOUT", -4: "ELIMIT"}
+
+
+class MoeNvfp4Error(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        name = _ERRNAMES.get(code, f"hipError {code}")
+        super().__init__(f"{fn} failed: {name} ({code})")
+        self.code = code
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("scale2", ctypes.c_void_p),
+        ("layout", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m nvfp4_quantized_moe_amd.build`"
+            )
+        L = ctypes.CDLL(str(LIB_PATH))
+        L.moe_nvfp4_sort.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_nvfp4_gate_up_silu.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _Experts, _P, _P, _P, _P, _P, _P]
+        L.moe_nvfp4_down.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _P, _P, _P, _P, _P]
+        L.moe_nvfp4_blend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
+        L.transpose_u8.argtypes = [_P, _P, _I, _I, _P]
+        for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
+                   "transpose_u8", "moe_nvfp4_abi_version"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions the C header declares."""
+    text = HEADER.read_text()
+    return re.findall(r"^\s*int\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MoeNvfp4Error(fn, rc)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+class ExpertTables:
+    """One NVFP4 projection across E experts: device arrays of the experts'
+    packed and scale pointers plus their f32 scale_2 values.  ``None`` in
+    ``weights`` marks an absent (NULL) expert."""
+
+    def __init__(self, weights: Sequence[Optional[tuple]], layout: int, device="cuda"):
+        packed, scales, s2 = [], [], []
+        self._keep = []
+        for w in weights:
+            if w is None:
+                packed.append(0)
+                scales.append(0)
+                s2.append(0.0)
+                continue
+            pk, sc, sv = w
+            packed.append(pk.data_ptr())
+            scales.append(sc.data_ptr())
+            s2.append(float(sv))
+            self._keep.append((pk, sc))
+        self.packed = torch.tensor(packed, dtype=torch.int64, device=device)
+        self.scale = torch.tensor(scales, dtype=torch.int64, device=device)
+        self.scale2 = torch.tensor(s2, dtype=torch.float32, device=device)
+        self.layout = int(layout)
+        self.E = len(weights)
+
+    def abi(self) -> _Experts:
+        return _Experts(self.packed.data_ptr(), self.scale.data_ptr(), self.scale2.data_ptr(), self.layout)
+
+
+# --------------------------------------------------------------------------
+# The five C entry points (argument marshalling only)
+# --------------------------------------------------------------------------
+def moe_nvfp4_sort(topk_ids, E, expert_offsets, sorted_token_ids, pair_pos, active_experts,
+                   active_count, err_flag, stream=None) -> None:
+    T, k = topk_ids.shape
+    rc = lib().moe_nvfp4_sort(
+        _dev(topk_ids, torch.int32, "topk_ids"), T, k, E,
+        _dev(expert_offsets, torch.int32, "expert_offsets"),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _dev(pair_pos, torch.int32, "pair_pos"),
+        _dev(active_experts, torch.int32, "active_experts"),
+        _dev(active_count, torch.int32, "active_count"),
+        _dev(err_flag, torch.int32, "err_flag"), _stream(stream))
+    _check("moe_nvfp4_sort", rc)
+
+
+def moe_nvfp4_gate_up_silu(x, k, E, H, I, gate: ExpertTables, up: ExpertTables, expert_offsets,
+                           sorted_token_ids, active_experts, active_count, h, stream=None) -> None:
+    T = x.shape[0]
+    rc = lib().moe_nvfp4_gate_up_silu(
+        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
+        T, k, E, H, I, gate.abi(), up.abi(),
+        _dev(expert_offsets, torch.int32, "expert_offsets"),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _dev(active_experts, torch.int32, "active_experts"),
+        _dev(active_count, torch.int32, "active_count"),
+        _dev(h, torch.float32, "h"), _stream(stream))
+    _check("moe_nvfp4_gate_up_silu", rc)
+
+
+def moe_nvfp4_down(h, T, k, E, H, I, down: ExpertTables, expert_offsets, active_experts, active_count,
+                   y, stream=None) -> None:
+    rc = lib().moe_nvfp4_down(
+        _dev(h, torch.float32, "h"), T, k, E, H, I, down.abi(),
+        _dev(expert_offsets, torch.int32, "expert_offsets"),
+        _dev(active_experts, torch.int32, "active_experts"),
+        _dev(active_count, torch.int32, "active_count"),
+        _dev(y, torch.float32, "y"), _stream(stream))
+    _check("moe_nvfp4_down", rc)
+
+
+def moe_nvfp4_blend(y, topk_weights, pair_pos, out, stream=None) -> None:
+    T, k = topk_weights.shape
+    H = y.shape[1]
+    rc = lib().moe_nvfp4_blend(
+        _dev(y, torch.float32, "y"), _dev(topk_weights, torch.float32, "topk_weights"),
+        _dev(pair_pos, torch.int32, "pair_pos"), T, k, H,
+        _dev(out, torch.bfloat16, "out") if out.dtype == torch.bfloat16 else _dev(out, torch.int16, "out"),
+        _stream(stream))
+    _check("moe_nvfp4_blend", rc)
+
+
+def transpose_u8(src, dst, rows, cols, stream=None) -> None:
+    if src.numel() != rows * cols or dst.numel() != rows * cols:
+        raise ValueError("transpose_u8: tensor sizes do not match rows * cols")
+    rc = lib().transpose_u8(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst"), rows, cols,
+                            _stream(stream))
+    _check("transpose_u8", rc)
+
+
+def transpose_for_gemm(packed: torch.Tensor, scale: torch.Tensor, n: int, k: int, group_size: int = 16):
+    """Load-time K-major twin (transpose.rs, transpose_for_gemm_gs): new
+    buffers packed [K/2, N] and scales [K/group, N]; the inputs are left
+    unchanged.  Both transposes run on the current stream, which is
+    synchronized before the twin is returned."""
+    pt = torch.empty((k // 2, n), dtype=torch.uint8, device=packed.device)
+    st = torch.empty((k // group_size, n), dtype=torch.uint8, device=scale.device)
+    transpose_u8(packed, pt, n, k // 2)
+    transpose_u8(scale, st, n, k // group_size)
+    torch.cuda.current_stream().synchronize()
+    return pt, st
+
+
+class MoeLayer:
+    """Device buffers and the four calls of one MoE layer forward.
+
+    ``gate``, ``up`` and ``down`` are ExpertTables (the same layout for all
+    three).  ``forward`` enqueues sort -> gate_up_silu -> down -> blend on
+    the current stream and returns the bf16 output [T, H]; the intermediate
+    buffers stay available as attributes for inspection.
+    """
+
+    def __init__(self, T: int, k: int, E: int, H: int, I: int, gate: ExpertTables, up: ExpertTables,
+                 down: ExpertTables, device="cuda"):
+        self.T, self.k, self.E, self.H, self.I = T, k, E, H, I
+        self.gate, self.up, self.down = gate, up, down
+        P = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.sorted_token_ids = torch.empty(P, **i32)
+        self.pair_pos = torch.empty(P, **i32)
+        self.active_experts = torch.empty(E, **i32)
+        self.active_count = torch.empty(1, **i32)
+        self.err_flag = torch.zeros(1, **i32)
+        self.h = torch.empty((P, I), dtype=torch.float32, device=device)
+        self.y = torch.empty((P, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+
+    def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, stream=None):
+        s = _stream(stream)
+        moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
+                       self.active_experts, self.active_count, self.err_flag, s)
+        moe_nvfp4_gate_up_silu(x, self.k, self.E, self.H, self.I, self.gate, self.up, self.expert_offsets,
+                               self.sorted_token_ids, self.active_experts, self.active_count, self.h, s)
+        moe_nvfp4_down(self.h, self.T, self.k, self.E, self.H, self.I, self.down, self.expert_offsets,
+                       self.active_experts, self.active_count, self.y, s)
+        moe_nvfp4_blend(self.y, topk_weights, self.pair_pos, self.out, s)
+        return self.out

@@ -1,0 +1,69 @@
+// C-ABI entry points of the two projection steps: host-side argument checks,
+// then one launch on the caller's stream.  The weight layout picks the
+// kernel: row-major -> decode GEMV (few rows per expert), K-major -> grouped
+// MFMA GEMM (many rows per expert), mirroring the pages' split between the
+// row-major decode kernels (nvfp4_moe_grouped.rs) and the transposed twins
+// built for the sorted prefill path (prefill_weights.rs).
+#include "moe_common.hpp"
+
+int moe_launch_gemv_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
+                        const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
+                        const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
+                        hipStream_t stream);
+int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
+                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
+                           const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
+                           hipStream_t stream);
+
+namespace {
+
+int check_common(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t layout) {
+    if (T < 1 || k < 1 || E < 1 || k > E || H < 1 || I < 1) return MOE_NVFP4_ESHAPE;
+    if (E > MOE_NVFP4_MAX_EXPERTS || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
+    if (H > MOE_NVFP4_MAX_WIDTH || I > MOE_NVFP4_MAX_WIDTH) return MOE_NVFP4_ELIMIT;
+    if (layout == MOE_NVFP4_ROW_MAJOR) {
+        if (H % 32 != 0 || I % 32 != 0) return MOE_NVFP4_ESHAPE;
+    } else if (layout == MOE_NVFP4_K_MAJOR) {
+        if (H % 64 != 0 || I % 64 != 0) return MOE_NVFP4_ESHAPE;
+    } else {
+        return MOE_NVFP4_ELAYOUT;
+    }
+    return MOE_NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
+                                      int32_t I, moe_nvfp4_experts gate, moe_nvfp4_experts up,
+                                      const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                                      const int32_t *active_experts, const int32_t *active_count, float *h,
+                                      void *stream) {
+    if (!x || !expert_offsets || !sorted_token_ids || !active_experts || !active_count || !h)
+        return MOE_NVFP4_ENULL;
+    if (moe_host::experts_null(gate) || moe_host::experts_null(up)) return MOE_NVFP4_ENULL;
+    if (gate.layout != up.layout) return MOE_NVFP4_ELAYOUT;
+    const int rc = check_common(T, k, E, H, I, gate.layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    const int P = T * k;
+    if (gate.layout == MOE_NVFP4_ROW_MAJOR)
+        return moe_launch_gemv_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
+                                   gate, &up, h, I, H, P, E, (hipStream_t)stream);
+    return moe_launch_gemm_kmajor(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
+                                  &up, h, I, H, P, E, (hipStream_t)stream);
+}
+
+extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                              moe_nvfp4_experts down, const int32_t *expert_offsets,
+                              const int32_t *active_experts, const int32_t *active_count, float *y,
+                              void *stream) {
+    if (!h || !expert_offsets || !active_experts || !active_count || !y) return MOE_NVFP4_ENULL;
+    if (moe_host::experts_null(down)) return MOE_NVFP4_ENULL;
+    const int rc = check_common(T, k, E, H, I, down.layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    const int P = T * k;
+    if (down.layout == MOE_NVFP4_ROW_MAJOR)
+        return moe_launch_gemv_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
+                                   nullptr, y, H, I, P, E, (hipStream_t)stream);
+    return moe_launch_gemm_kmajor(false, h, nullptr, expert_offsets, active_experts, active_count, down,
+                                  nullptr, y, H, I, P, E, (hipStream_t)stream);
+}

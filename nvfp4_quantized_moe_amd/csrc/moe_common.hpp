@@ -1,0 +1,103 @@
+// Shared device helpers and host argument checks for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_nvfp4.h"
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Format decode.  gfx950's scaled converters apply only the exponent of the
+// f32 scale operand, so they are called with 1.0 and the E4M3 block scale is
+// applied separately.  Both conversions are exact: every E2M1 value is a
+// bf16/fp16 number and the OCP E4M3 codes convert exactly to f32.
+// ---------------------------------------------------------------------------
+
+// Byte B of w holds two E2M1 codes; low nibble -> .x (even k), high -> .y.
+template <int B>
+__device__ __forceinline__ bf16x2_t e2m1x2_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ f16x2_t e2m1x2_f16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
+}
+// Byte B of w as an E4M3 (OCP FN) code, widened to f32.
+template <int B>
+__device__ __forceinline__ float e4m3_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_f32_fp8(w, B);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+template <typename T, typename U>
+__device__ __forceinline__ T bitcast(U u) {
+    static_assert(sizeof(T) == sizeof(U), "size");
+    T t;
+    __builtin_memcpy(&t, &u, sizeof(T));
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums with DPP (within 16-lane rows).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+
+// Sum over aligned groups of L lanes (L in {1,2,4,8,16}); every lane of the
+// group receives the group total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (L >= 2) v += dpp<kDppXor1>(v);
+    if constexpr (L >= 4) v += dpp<kDppXor2>(v);
+    if constexpr (L >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (L >= 16) v += dpp<kDppMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float silu_f32(float z) {
+    return z / (1.0f + __expf(-z));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Host-side helpers.
+// ---------------------------------------------------------------------------
+namespace moe_host {
+
+inline bool experts_null(const moe_nvfp4_experts &w) {
+    return w.packed == nullptr || w.scale == nullptr || w.scale2 == nullptr;
+}
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_NVFP4_OK : (int)e;
+}
+
+}  // namespace moe_host

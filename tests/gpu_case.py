@@ -1,0 +1,101 @@
+"""Device-side test cases built from the seeded generators.
+
+A ``Case`` uploads one workload's inputs (x, routing, the experts' NVFP4
+weights) to the GPU, builds the pointer tables, and runs the four C-ABI
+calls through ``MoeLayer``.  The oracle side regenerates any expert's bytes
+from the same seeds on the CPU (``weight_fn``), so only what a check needs is
+ever dequantised.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import nvfp4_quantized_moe_amd as moe
+import synth
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Case:
+    def __init__(self, cfg_id: int, shape: synth.MoeShape | None = None, nulls=(), kmajor: bool | None = None,
+                 ids: np.ndarray | None = None, weights: np.ndarray | None = None, all_experts: bool = False):
+        self.cfg_id = cfg_id
+        self.shape = shape or synth.config(cfg_id)
+        s = self.shape
+        self.kmajor = s.kmajor if kmajor is None else kmajor
+        self.x_bits = synth.gen_x(cfg_id, s)
+        gids, gw = synth.gen_routing(cfg_id, s)
+        self.ids = gids if ids is None else ids.astype(np.int32)
+        self.w = gw if weights is None else weights.astype(np.float32)
+        self.nulls = set(nulls)
+        flat = self.ids.reshape(-1)
+        self.active = sorted({int(e) for e in flat if 0 <= e < s.E})
+        need = range(s.E) if all_experts else self.active
+        self.dev = {}
+        for e in need:
+            if e in self.nulls:
+                continue
+            for proj in (0, 1, 2):
+                n, k = synth.proj_dims(s, proj)
+                pk, sc = synth.gen_expert(cfg_id, e, proj, s)
+                pk_d = torch.from_numpy(pk).cuda()
+                sc_d = torch.from_numpy(sc).cuda()
+                if self.kmajor:
+                    pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k)
+                self.dev[(e, proj)] = (pk_d, sc_d)
+        layout = moe.K_MAJOR if self.kmajor else moe.ROW_MAJOR
+        self.scale2 = {p: np.float32(synth.SCALE2_F32) for p in (0, 1, 2)}
+        self.tables = [self._table(p, layout) for p in (0, 1, 2)]
+        self.x = torch.from_numpy(self.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        self.ids_d = torch.from_numpy(self.ids).cuda()
+        self.w_d = torch.from_numpy(self.w).cuda()
+        self.layer = moe.MoeLayer(s.T, s.k, s.E, s.H, s.I, *self.tables)
+
+    def _table(self, proj, layout):
+        rows = []
+        for e in range(self.shape.E):
+            t = self.dev.get((e, proj))
+            rows.append(None if t is None else (t[0], t[1], self.scale2[proj]))
+        return moe.ExpertTables(rows, layout)
+
+    def set_scale2(self, proj: int, value: float):
+        self.scale2[proj] = np.float32(value)
+        layout = moe.K_MAJOR if self.kmajor else moe.ROW_MAJOR
+        self.tables[proj] = self._table(proj, layout)
+        self.layer.gate, self.layer.up, self.layer.down = self.tables
+
+    # oracle-side weights (row-major numpy, regenerated from the seeds)
+    def weight_fn(self):
+        s = self.shape
+
+        def fn(e, proj):
+            if e in self.nulls:
+                return None
+            pk, sc = synth.gen_expert(self.cfg_id, e, proj, s)
+            return pk, sc, self.scale2[proj]
+
+        return fn
+
+    def run(self):
+        self.layer.err_flag.zero_()
+        out = self.layer.forward(self.x, self.ids_d, self.w_d)
+        torch.cuda.synchronize()
+        return out
+
+    def sort_outputs(self) -> dict:
+        L = self.layer
+        n = int(L.active_count.item())
+        return {
+            "expert_offsets": L.expert_offsets.cpu().numpy(),
+            "sorted_token_ids": L.sorted_token_ids.cpu().numpy(),
+            "pair_pos": L.pair_pos.cpu().numpy(),
+            "active_experts": L.active_experts.cpu().numpy(),
+            "active_count": n,
+            "err": int(L.err_flag.item()),
+        }

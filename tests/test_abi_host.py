@@ -1,0 +1,78 @@
+"""The C-ABI library on the host: it loads, exports every declared entry
+point, and rejects bad arguments before launching anything (CPU only: every
+call below fails the host-side check, so no GPU work is enqueued)."""
+import ctypes
+
+import pytest
+
+import nvfp4_quantized_moe_amd as moe
+from nvfp4_quantized_moe_amd import _Experts
+
+ENULL, ESHAPE, ELAYOUT, ELIMIT = -1, -2, -3, -4
+D = 0x1000  # a non-NULL dummy address, never dereferenced on these paths
+
+
+def test_library_exports_every_header_function():
+    L = moe.lib()
+    names = moe.header_functions()
+    assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
+                          "transpose_u8", "moe_nvfp4_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_nvfp4_abi_version() == 1
+
+
+def _ex(layout=0, null=False):
+    return _Experts(0 if null else D, D, D, layout)
+
+
+def test_sort_rejects():
+    L = moe.lib()
+    ok = [D, 4, 2, 4, D, D, D, D, D, D, None]
+    for i in (0, 4, 5, 6, 7, 8, 9):
+        a = list(ok)
+        a[i] = None
+        assert L.moe_nvfp4_sort(*a) == ENULL
+    assert L.moe_nvfp4_sort(D, 0, 2, 4, D, D, D, D, D, D, None) == ESHAPE
+    assert L.moe_nvfp4_sort(D, 4, 0, 4, D, D, D, D, D, D, None) == ESHAPE
+    assert L.moe_nvfp4_sort(D, 4, 5, 4, D, D, D, D, D, D, None) == ESHAPE    # k > E
+    assert L.moe_nvfp4_sort(D, 4, 2, 2000, D, D, D, D, D, D, None) == ELIMIT
+    assert L.moe_nvfp4_sort(D, 1 << 21, 8, 16, D, D, D, D, D, D, None) == ELIMIT
+
+
+def test_gate_up_rejects():
+    L = moe.lib()
+
+    def call(x=D, T=4, k=2, E=4, H=256, I=512, g=None, u=None, h=D):
+        return L.moe_nvfp4_gate_up_silu(x, T, k, E, H, I, g or _ex(), u or _ex(), D, D, D, D, h, None)
+
+    assert call(x=None) == ENULL
+    assert call(h=None) == ENULL
+    assert call(g=_ex(null=True)) == ENULL
+    assert call(g=_ex(0), u=_ex(1)) == ELAYOUT
+    assert call(g=_ex(7), u=_ex(7)) == ELAYOUT
+    assert call(H=48) == ESHAPE                         # row-major needs H % 32 == 0
+    assert call(I=528, g=_ex(1), u=_ex(1)) == ESHAPE    # K-major needs I % 64 == 0
+    assert call(k=5) == ESHAPE
+    assert call(H=1 << 17) == ELIMIT
+
+
+def test_down_and_blend_and_transpose_reject():
+    L = moe.lib()
+    assert L.moe_nvfp4_down(None, 4, 2, 4, 256, 512, _ex(), D, D, D, D, None) == ENULL
+    assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 512, _ex(null=True), D, D, D, D, None) == ENULL
+    assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 500, _ex(), D, D, D, D, None) == ESHAPE
+    assert L.moe_nvfp4_blend(D, D, None, 4, 2, 256, D, None) == ENULL
+    assert L.moe_nvfp4_blend(D, D, D, 0, 2, 256, D, None) == ESHAPE
+    assert L.moe_nvfp4_blend(D, D, D, 4, 2, 1 << 17, D, None) == ELIMIT
+    assert L.transpose_u8(None, D, 4, 4, None) == ENULL
+    assert L.transpose_u8(D, D, 0, 4, None) == ESHAPE
+
+
+def test_python_binding_checks_tensor_arguments():
+    import torch
+
+    with pytest.raises(ValueError):
+        moe.transpose_u8(torch.zeros(4, dtype=torch.uint8), torch.zeros(4, dtype=torch.uint8), 2, 3)
+    with pytest.raises((TypeError, ValueError)):
+        moe.transpose_u8(torch.zeros(6, dtype=torch.uint8), torch.zeros(6, dtype=torch.uint8), 2, 3)
