@@ -1,0 +1,277 @@
+"""Benchmark of the grouped NVFP4 MoE expert projection on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--eager]
+
+A step is one MoE layer forward through the whole path — routing sort,
+gate+up+SiLU, down, blend — over one batch of synthetic input.  Every input
+is resident in HBM before timing starts.  Consecutive steps run different
+layers' expert weights (separate HBM copies, as successive layers of a model
+would), so the weights a step reads were last touched far more than the
+256 MB Infinity Cache ago: the measured bandwidth is HBM bandwidth.
+
+The K timed steps are captured into one HIP graph and replayed once, between
+a device synchronisation on each side (``--eager`` launches them one by one
+instead).  Reported on one JSON line:
+  value       expert-weight bytes of the active experts per step / step time (GB/s)
+  tokens_per_s, pct_of_hbm_peak
+  roofline    the dominant kernel (gate+up+SiLU): its algorithmic bytes per
+              launch / its mean launch duration, timed with HIP events on the
+              stream it runs on, against 8 TB/s
+  cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
+              same workload, in the same unit
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "expert-weight HBM GB/s (% of peak) + MoE-layer tokens/s, decode batch 1/32"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (2 = decode, 1 token)")
+    ap.add_argument("--layers", type=int, default=0, help="weight copies cycled over (0 = auto)")
+    ap.add_argument("--batches", type=int, default=8, help="distinct routing batches cycled over")
+    ap.add_argument("--eager", action="store_true", help="launch step by step instead of one graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def active_weight_bytes(shape, ids) -> int:
+    import synth
+
+    act = np.unique(ids[(ids >= 0) & (ids < shape.E)])
+    return int(act.size) * synth.expert_bytes(shape)
+
+
+def gate_up_bytes(shape, ids) -> int:
+    """Algorithmic bytes of one gate+up launch: the active experts' gate and up
+    weights (packed + scales), x read once, h written once, 4-byte scale_2s."""
+    act = np.unique(ids[(ids >= 0) & (ids < shape.E)]).size
+    w = act * 2 * (shape.I * shape.H // 2 + shape.I * shape.H // 16 + 4)
+    return int(w + shape.T * shape.H * 2 + shape.P * shape.I * 4)
+
+
+def cpu_baseline(shape, cfg_id, seconds):
+    """Time the fp64 oracle on a bounded sample: whole layer forwards of the
+    same workload (tokens sampled down for the many-token workload)."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = int(max(blas)) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    T = shape.T if shape.T <= 64 else 64
+    sub = synth.MoeShape(shape.name + "_cpu", T, shape.H, shape.I, shape.E, shape.k, shape.routing, False,
+                         shape.zipf_s)
+
+    def wf(e, proj):
+        pk, sc = synth.gen_expert(cfg_id, e, proj, shape)
+        return pk, sc, synth.SCALE2_F32
+
+    done_tokens, done_bytes, t_used, runs = 0, 0, 0.0, 0
+    b = 0
+    while t_used < seconds and runs < 50:
+        x = synth.gen_x(cfg_id, shape, batch=b)[:T]
+        ids, w = synth.gen_routing(cfg_id, shape, batch=b)
+        ids, w = ids[:T], w[:T]
+        # weight bytes are generated outside the timed region; decode + compute inside
+        cache = {}
+        for e in np.unique(ids):
+            for p in (0, 1, 2):
+                cache[(int(e), p)] = wf(int(e), p)
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, ids, w, lambda e, p: cache[(e, p)], sub.E, sub.H, sub.I)
+        t_used += time.perf_counter() - t0
+        done_tokens += T
+        done_bytes += active_weight_bytes(sub, ids)
+        runs += 1
+        b += 1
+    return {
+        "value": round(done_bytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(done_tokens / t_used, 3),
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{runs} fp64 oracle layer forwards of {T} token(s) each (dequant + sort + gate/up + down + blend, "
+                  f"weights generated outside the timing), {t_used:.1f} s of CPU time; numpy elementwise work on "
+                  f"1 thread, BLAS on up to {cores}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_quantized_moe_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py: no GPU")
+    moe.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    cfg_id = args.workload
+    shape = synth.config(cfg_id)
+    layout = moe.K_MAJOR if shape.kmajor else moe.ROW_MAJOR
+
+    # ---- inputs: R routing batches, L layers of expert weights -----------
+    R = max(1, args.batches)
+    xs, idss, ws = [], [], []
+    for b in range(R):
+        xs.append(torch.from_numpy(synth.gen_x(cfg_id, shape, batch=b).view(np.int16)).to(dev).view(torch.bfloat16))
+        ids, w = synth.gen_routing(cfg_id, shape, batch=b)
+        idss.append(ids)
+        ws.append(w)
+    ids_d = [torch.from_numpy(i).to(dev) for i in idss]
+    w_d = [torch.from_numpy(w).to(dev) for w in ws]
+    step_bytes = [active_weight_bytes(shape, i) for i in idss]
+    all_bytes = shape.E * synth.expert_bytes(shape)
+    if args.layers > 0:
+        L = args.layers
+    else:
+        L = max(1, math.ceil(2.0e9 / min(step_bytes)))
+        L = min(L, 64, max(1, int(48e9 // all_bytes)))
+    base = {}
+    for e in range(shape.E):
+        for p in (0, 1, 2):
+            n, k = synth.proj_dims(shape, p)
+            pk, sc = synth.gen_expert(cfg_id, e, p, shape)
+            pk_d, sc_d = torch.from_numpy(pk).to(dev), torch.from_numpy(sc).to(dev)
+            if shape.kmajor:
+                pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k)
+            base[(e, p)] = (pk_d, sc_d)
+    layers = []
+    for li in range(L):
+        wts = base if li == 0 else {key: (a.clone(), b.clone()) for key, (a, b) in base.items()}
+        tabs = [moe.ExpertTables([(wts[(e, p)][0], wts[(e, p)][1], synth.SCALE2_F32) for e in range(shape.E)],
+                                 layout, device=dev) for p in (0, 1, 2)]
+        layers.append((wts, tabs))
+    bufs = moe.MoeLayer(shape.T, shape.k, shape.E, shape.H, shape.I, *layers[0][1], device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def step(i, s):
+        bufs.gate, bufs.up, bufs.down = layers[i % L][1]
+        b = i % R
+        bufs.forward(xs[b], ids_d[b], w_d[b], stream=s)
+
+    def run_steps(first, n, s):
+        for i in range(first, first + n):
+            step(i, s)
+
+    K, W = args.steps, args.warmup
+    with torch.cuda.stream(stream):
+        run_steps(0, min(W, 3), stream)  # plain warm launch before any capture
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    if args.eager:
+        with torch.cuda.stream(stream):
+            run_steps(0, W, stream)
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            run_steps(W, K, stream)
+            t_end.record(stream)
+        torch.cuda.synchronize()
+    else:
+        g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream):
+            run_steps(0, max(W, 1), stream)
+        with torch.cuda.graph(g_main, stream=stream):
+            run_steps(W, K, stream)
+        torch.cuda.synchronize()
+        g_warm.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            t_start.record(stream)
+            g_main.replay()
+            t_end.record(stream)
+        torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    bytes_timed = sum(step_bytes[i % R] for i in range(W, W + K))
+    value = bytes_timed / (total_ms / 1e3) / 1e9
+    tokens_per_s = shape.T * K / (total_ms / 1e3)
+
+    # ---- dominant kernel: gate+up+SiLU launch duration (HIP events on its stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            bufs.gate, bufs.up, bufs.down = layers[i % L][1]
+            b = i % R
+            moe.moe_nvfp4_sort(ids_d[b], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
+                               bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
+            ev[i][0].record(stream)
+            moe.moe_nvfp4_gate_up_silu(xs[b], shape.k, shape.E, shape.H, shape.I, bufs.gate, bufs.up,
+                                       bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
+                                       bufs.active_count, bufs.h, stream)
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gu_bytes = float(np.mean([gate_up_bytes(shape, idss[i % R]) for i in range(K)]))
+    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name,
+            "tokens": shape.T, "hidden": shape.H, "expert_inter": shape.I, "experts": shape.E, "top_k": shape.k,
+            "routing": shape.routing, "weight_layout": "k_major" if shape.kmajor else "row_major",
+            "weight_copies_cycled": L, "routing_batches_cycled": R,
+            "launch": "eager" if args.eager else "hip_graph",
+        },
+        "tokens_per_s": round(tokens_per_s, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "active_weight_bytes_per_step": round(bytes_timed / K),
+        "roofline": {
+            "kernel": "moe_nvfp4_gate_up_silu",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": round(gu_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": round(gu_bytes),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(shape, cfg_id, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

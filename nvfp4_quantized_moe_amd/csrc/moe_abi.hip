@@ -1,15 +1,14 @@
 // C-ABI entry points of the two projection steps: host-side argument checks,
 // then one launch on the caller's stream.  The weight layout picks the
-// kernel: row-major -> decode GEMV (few rows per expert), K-major -> grouped
+// kernel: row-major -> decode kernel (few rows per expert), K-major -> grouped
 // MFMA GEMM (many rows per expert), mirroring the pages' split between the
 // row-major decode kernels (nvfp4_moe_grouped.rs) and the transposed twins
 // built for the sorted prefill path (prefill_weights.rs).
 #include "moe_common.hpp"
 
-int moe_launch_gemv_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
-                        const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
-                        const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
-                        hipStream_t stream);
+int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
+                          const int32_t *active, const moe_nvfp4_experts &A, const moe_nvfp4_experts *B,
+                          float *out, int N, int K, int P, int E, hipStream_t stream);
 int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                            const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                            const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
@@ -46,8 +45,8 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
     if (rc != MOE_NVFP4_OK) return rc;
     const int P = T * k;
     if (gate.layout == MOE_NVFP4_ROW_MAJOR)
-        return moe_launch_gemv_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
-                                   gate, &up, h, I, H, P, E, (hipStream_t)stream);
+        return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, gate, &up, h,
+                                     I, H, P, E, (hipStream_t)stream);
     return moe_launch_gemm_kmajor(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
                                   &up, h, I, H, P, E, (hipStream_t)stream);
 }
@@ -62,8 +61,8 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
     if (rc != MOE_NVFP4_OK) return rc;
     const int P = T * k;
     if (down.layout == MOE_NVFP4_ROW_MAJOR)
-        return moe_launch_gemv_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
-                                   nullptr, y, H, I, P, E, (hipStream_t)stream);
+        return moe_launch_decode_row(false, h, nullptr, expert_offsets, active_experts, down, nullptr, y, H, I,
+                                     P, E, (hipStream_t)stream);
     return moe_launch_gemm_kmajor(false, h, nullptr, expert_offsets, active_experts, active_count, down,
                                   nullptr, y, H, I, P, E, (hipStream_t)stream);
 }

@@ -42,6 +42,35 @@ __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
 
+// Loads through pointers known to be in global memory.  Pointers read from a
+// table (the per-expert weight pointers) are generic to the compiler, which
+// would otherwise emit flat loads; those count against both the vector-memory
+// and the LDS counters and force conservative waits.
+// (HIP's uint4/float4 are structs whose copies go through a generic memcpy,
+// so 16-byte values move as a native 4 x u32 vector.)
+#define MOE_GLOBAL __attribute__((address_space(1)))
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+template <typename T>
+__device__ __forceinline__ T gload(const void *p) {
+    if constexpr (sizeof(T) == 16) {
+        const u32x4_t v = *(const MOE_GLOBAL u32x4_t *)p;
+        T t;
+        __builtin_memcpy(&t, &v, 16);
+        return t;
+    } else if constexpr (sizeof(T) == 8) {
+        const u32x2_t v = *(const MOE_GLOBAL u32x2_t *)p;
+        T t;
+        __builtin_memcpy(&t, &v, 8);
+        return t;
+    } else {
+        return *(const MOE_GLOBAL T *)p;
+    }
+}
+
+// Index of this wavefront in the block, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 template <typename T, typename U>
 __device__ __forceinline__ T bitcast(U u) {
     static_assert(sizeof(T) == sizeof(U), "size");

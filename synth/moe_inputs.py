@@ -4,8 +4,8 @@ Every array is drawn from numpy's PCG64 under
 ``SeedSequence([2026, cfg_id, tag, a, b])`` so that any single expert
 projection can be regenerated on its own:
 
-    tag 1  activations x                (a = b = 0)
-    tag 2  router logits                (a = b = 0)
+    tag 1  activations x                (a = batch, b = 0)
+    tag 2  router logits                (a = batch, b = 0)
     tag 3  Zipf rank permutation        (a = b = 0)
     tag 4  packed E2M1 bytes            (a = expert, b = projection)
     tag 5  E4M3 block-scale codes       (a = expert, b = projection)
@@ -93,17 +93,19 @@ def expert_bytes(shape: MoeShape) -> int:
     return tot
 
 
-def gen_x(cfg_id: int, shape: MoeShape | None = None) -> np.ndarray:
-    """Activations as bf16 bit patterns, uint16 [T, H]."""
+def gen_x(cfg_id: int, shape: MoeShape | None = None, batch: int = 0) -> np.ndarray:
+    """Activations as bf16 bit patterns, uint16 [T, H]; ``batch`` selects an
+    independent draw of the same workload."""
     shape = shape or config(cfg_id)
-    f = _rng(cfg_id, 1).standard_normal((shape.T, shape.H), dtype=np.float32)
+    f = _rng(cfg_id, 1, batch).standard_normal((shape.T, shape.H), dtype=np.float32)
     return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def gen_routing(cfg_id: int, shape: MoeShape | None = None):
-    """Router output: (topk_ids int32 [T, k], topk_weights float32 [T, k])."""
+def gen_routing(cfg_id: int, shape: MoeShape | None = None, batch: int = 0):
+    """Router output: (topk_ids int32 [T, k], topk_weights float32 [T, k]);
+    ``batch`` selects an independent draw (the Zipf rank order is shared)."""
     shape = shape or config(cfg_id)
-    logits = _rng(cfg_id, 2).standard_normal((shape.T, shape.E))
+    logits = _rng(cfg_id, 2, batch).standard_normal((shape.T, shape.E))
     if shape.routing == "zipf":
         rank = 1 + _rng(cfg_id, 3).permutation(shape.E)
         logits = logits - shape.zipf_s * np.log(rank.astype(np.float64))[None, :]
