@@ -135,8 +135,9 @@ int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
  *                     moe_nvfp4_sort's outputs (read on the device only).
  *   h                 out fp32 [P, I]; rows of positions that belong to no
  *                     active expert are left untouched.
- * Admission: H % 32 == 0 and I % 32 == 0 (ROW_MAJOR); H % 64 == 0 and
- * I % 64 == 0 (K_MAJOR).  The K_MAJOR path feeds the matrix cores with fp16
+ * Admission: H % 64 == 0 and I % 64 == 0 (both layouts), H >= 256 and
+ * I >= 256 (ROW_MAJOR); packed, scale and activation buffers 16-byte
+ * aligned.  The K_MAJOR path feeds the matrix cores with fp16
  * operands, so it admits activations of magnitude below 65504.
  * Errors: ENULL, ESHAPE, ELAYOUT, ELIMIT (E, P or width above the maxima).
  */

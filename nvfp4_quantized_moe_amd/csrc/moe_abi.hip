@@ -20,13 +20,9 @@ int check_common(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t 
     if (T < 1 || k < 1 || E < 1 || k > E || H < 1 || I < 1) return MOE_NVFP4_ESHAPE;
     if (E > MOE_NVFP4_MAX_EXPERTS || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
     if (H > MOE_NVFP4_MAX_WIDTH || I > MOE_NVFP4_MAX_WIDTH) return MOE_NVFP4_ELIMIT;
-    if (layout == MOE_NVFP4_ROW_MAJOR) {
-        if (H % 32 != 0 || I % 32 != 0) return MOE_NVFP4_ESHAPE;
-    } else if (layout == MOE_NVFP4_K_MAJOR) {
-        if (H % 64 != 0 || I % 64 != 0) return MOE_NVFP4_ESHAPE;
-    } else {
-        return MOE_NVFP4_ELAYOUT;
-    }
+    if (layout != MOE_NVFP4_ROW_MAJOR && layout != MOE_NVFP4_K_MAJOR) return MOE_NVFP4_ELAYOUT;
+    if (H % 64 != 0 || I % 64 != 0) return MOE_NVFP4_ESHAPE;
+    if (layout == MOE_NVFP4_ROW_MAJOR && (H < 256 || I < 256)) return MOE_NVFP4_ESHAPE;
     return MOE_NVFP4_OK;
 }
 

@@ -1,54 +1,71 @@
 // Decode path: grouped NVFP4 projection over row-major weights (packed
 // [N, K/2], scales [N, K/16]) for the few tokens routed to each expert.
 //
-// nvfp4_moe_grouped.rs, docs of moe_expert_gate_up_act_nvfp4_grouped and
-// moe_expert_down_act_nvfp4_grouped: one block row per active-expert slot
+// Grouped NVFP4 MoE decode kernels (moe_expert_gate_up_act_nvfp4_grouped and
+// moe_expert_down_act_nvfp4_grouped): one block row per active-expert slot
 // (grid y = cap = min(E, P)); blocks past the device-side active count exit;
 // gate+up fuse the SiLU product into fp32 h[position, n]; down reads h and
 // writes fp32 y[position, n].
 //
-// gfx950 mapping.  A block owns one unit of 32 weight rows (gate+up: 16
-// columns of each matrix; down: 32 columns) of one expert and streams those
-// rows' packed bytes once.  The unit's E4M3 scales are staged in LDS first,
-// so the only vector-memory loads in the inner loops are the 16-byte weight
-// chunks (and, on the matrix-core path, the activation chunks that travel
-// with them): the loops refill a ring of them without branching, which keeps
-// the waits partial and several chunks in flight per lane.  The block picks
-// one of two code paths from the expert's row count (uniform over the block):
+// gfx950 mapping.  The projection is bound by streaming the expert weights
+// from HBM, so the kernel is laid out around one rule: in the steady state
+// the only global loads are the weight stream itself, each instruction
+// covering 4 rows x 256 contiguous bytes, plus one 16-byte-per-lane load of
+// the matching E4M3 scales every four steps.  Everything else a step needs
+// comes from LDS.
 //
-//   one routed row  -> VALU GEMV.  16 groups of 16 lanes; group g owns the
-//     row pair (g, g+16) (gate and up of one column, or two down columns),
-//     lane j of the group the 16-byte chunks j, j+16, ... of the K axis.
-//     The activation row is staged in LDS as bf16.  E2M1 -> f32 pairs with the
-//     hardware converter, fp32 FMAs, the E4M3 scale applied once per 16
-//     products, the 16 partial sums combined with DPP.
-//
-//   2 .. n rows     -> matrix cores, 16x16x32 bf16 MFMA in passes of 16 rows.
-//     The 4 waves split the K axis (wave w takes K-tiles w, w+4, ... of 128
-//     k); lane (r, q) decodes the 16-byte chunk of row pair (r, r+16) at
-//     k = tile*128 + 32q straight into its B operands (E2M1 -> f32 pairs,
-//     times the E4M3 scale, -> bf16: exact) and loads the same 32 k of
-//     activation row r as its A operands (bf16 x as is; fp32 h rounded to
-//     bf16).  The four waves' partial tiles are summed through LDS.  Decoding
-//     each weight once per pass keeps the VALU work per weight byte
-//     independent of the row count, which a GEMV does not (its FMAs grow with
-//     the rows).
+//   * Work split.  The weight rows of an expert are cut into units of 32 rows
+//     (gate+up: 16 output columns of each matrix; down: 32 output columns); a
+//     block streams G consecutive units (G from the shape on the host).  Wave
+//     w of the block owns 8 rows of every unit, as two groups of 4 (gate+up:
+//     the gate rows and the up rows of the same 4 columns), over the whole K
+//     axis, so no partial sums cross waves.
+//   * Ring.  A wave walks its rows segment by segment (512 k = 256 bytes per
+//     row): per segment ("step"), two 16-byte loads per lane, one per row
+//     group.  Steps flow through a register ring of depth D that is refilled
+//     without any branch around the loads and in a pinned issue order, so the
+//     waits on it stay partial and the ring runs on across unit boundaries.
+//     Steps past the end of the stream repeat the last real address (a cache
+//     hit) and contribute nothing; lanes of a ragged last segment read a
+//     valid chunk of the same row and contribute zero.
+//   * Scales.  Every fourth step also loads the scale slices of the next four
+//     steps, 16 bytes per lane (8 rows x 4 steps x 32 bytes), into a 1 KiB
+//     LDS area of the wave; each step reads its two scale bytes per lane from
+//     there.
+//   * Matrix cores.  16x16x32 fp16 MFMA.  Lane (n, q) (n = lane & 15, q =
+//     lane >> 4) holds 16 bytes of row n >> 2 at byte 64q + 16(n & 3) of the
+//     segment: each B column is one (row, quarter) pair, so an instruction
+//     reads 256 contiguous bytes per row.  The A rows are (token, quarter)
+//     pairs, 4 tokens per MFMA, fed with the activation at the same k.  Only
+//     the blocks where the two quarters agree are kept, and the 4 quarters are
+//     summed across a quad of lanes at the end of the unit.  The E2M1 codes
+//     are widened to fp16 pairs and multiplied by the E4M3 scale in fp16
+//     (exact: at most 6 significant bits, range 2^-10 .. 2688).  A pass
+//     handles up to 16 routed rows (4 MFMA token groups) sharing each decoded
+//     weight; experts with more rows than the staged activation holds take
+//     further passes.
+//   * Activations.  LDS holds the pass's activation rows (x rows for gate+up,
+//     h rows for down) as fp16, each row scaled by a power of two that brings
+//     its largest magnitude into [2^14, 2^15): x (bf16) is then exact for
+//     every element down to 2^-29 of the row maximum and h keeps 11
+//     significant bits, whatever the row's range.  The factor is undone in
+//     the epilogue.  The row stride is padded so the A-operand reads are free
+//     of bank conflicts.
 #include "moe_common.hpp"
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / moe::kWave;
-constexpr int kUnitRows = 32;  // weight rows per block
-constexpr int kKT = 128;       // k per MFMA K-tile: one 16-byte chunk per lane group
-constexpr int kDepth = 6;      // VALU path: chunks in flight per lane and row
-constexpr int kRing = 3;       // MFMA path: K-tiles in flight per wave
-constexpr int kPassRows = 16;  // MFMA path: rows per pass (one 16-row tile)
-constexpr int kRedBytes = kWaves * 2 * 4 * 64 * (int)sizeof(float);  // MFMA partial tiles
+constexpr int kDepth = 4;          // ring: steps in flight per wave (a multiple of kGroup)
+constexpr int kGroup = 4;          // steps per scale load
+constexpr int kSegBytes = 256;     // bytes of one weight row per step (512 k)
+constexpr int kMaxTG = 4;          // token groups of 4 per pass (16 rows)
+constexpr int kLdsBudget = 72 * 1024;  // staged activation rows per block (two blocks per CU)
+constexpr int kScaleLds = 1024;        // per wave: 4 steps x 8 rows x 32 bytes
+constexpr int kHdrLds = kWaves * kScaleLds + 64;  // scale areas + per-row maxima
 
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v_t;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+using moe::u32x4_t;
 
 struct DecArgs {
     const void *act;            // gate+up: bf16 x [T, K]; down: fp32 h [P, K]
@@ -63,336 +80,366 @@ struct DecArgs {
     const float *s2b;
     float *out;                 // [P, N]
     int N, K;
+    int G;                      // units per block
+    int units;                  // units along N
+    int pass_rows;              // activation rows staged per pass
+    int ldx;                    // staged row stride, fp16 elements
 };
 
-template <int B>
-__device__ __forceinline__ f32x2_t e2m1x2_f32(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+// 8 E2M1 codes (one 32-bit word: k .. k+7) times the block scale, as fp16.
+__device__ __forceinline__ f16x8_t decode_b(uint32_t w, f16x2_t s) {
+    const f16x2_t v0 = moe::e2m1x2_f16<0>(w) * s, v1 = moe::e2m1x2_f16<1>(w) * s;
+    const f16x2_t v2 = moe::e2m1x2_f16<2>(w) * s, v3 = moe::e2m1x2_f16<3>(w) * s;
+    f16x8_t r;
+    r[0] = v0.x;
+    r[1] = v0.y;
+    r[2] = v1.x;
+    r[3] = v1.y;
+    r[4] = v2.x;
+    r[5] = v2.y;
+    r[6] = v3.x;
+    r[7] = v3.y;
+    return r;
 }
 
-// The unit's 32 scale rows -> LDS, row rho at sl + rho * (K/16).  Rows of one
-// matrix are consecutive in memory (16 or 32 rows of K/16 bytes each), so the
-// copy is one or two contiguous runs of 16-byte units.
+__device__ __forceinline__ float pick(const f32x4_t &v, int i) {
+    float r = v[0];
+    r = i == 1 ? v[1] : r;
+    r = i == 2 ? v[2] : r;
+    r = i == 3 ? v[3] : r;
+    return r;
+}
+
+// Power-of-two exponent e that brings a row maximum (bits of a non-negative
+// float) into [2^14, 2^15) after scaling by 2^-e; 0 for zero, inf or NaN.
+__device__ __forceinline__ int row_exp(uint32_t mbits) {
+    const int ef = (int)(mbits >> 23);
+    if (mbits == 0u || ef >= 255) return 0;
+    const int e = (ef == 0 ? -126 : ef - 127) - 14;
+    return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float absmax8(uint4 v) {
+    const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+    const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+    return fmaxf(a, b);
+}
+
+// Gate+up: rows [row0, row0 + pr) of x -> LDS as bf16 (stride ldx), each
+// row's largest magnitude max-ed into rmax[m] (float bits).  Lane m < 16 of
+// each wave holds the token of row m in tokv.
+// Down: only the maxima of rows [row0, row0 + pr) of h.
 template <bool GATED>
-__device__ __forceinline__ void stage_scales(int K, int n0, const uint8_t *sA, const uint8_t *sB, uint8_t *sl) {
-    const int rowb = K >> 4;
+__device__ __forceinline__ void stage_rows(const DecArgs &a, int row0, int pr, int tokv, uint16_t *xs,
+                                           uint32_t *rmax) {
+    const int K = a.K, ldx = a.ldx;
+    const int cpr = K >> 3;  // 8-element chunks per row
+    const int nch = pr * cpr;
+    constexpr int SB = GATED ? 8 : 4;  // chunks per thread per batch
+    for (int base = 0; base < nch; base += kThreads * SB) {
+        int row[SB];
+        float mx[SB];
+        if constexpr (GATED) {
+            int dst[SB];
+            u32x4_t raw[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int idx = base + i * kThreads + (int)threadIdx.x;
+                const int ic = idx < nch ? idx : 0;
+                const int m = ic / cpr, kc = ic - m * cpr;
+                row[i] = m;
+                dst[i] = m * ldx + 8 * kc;
+                const int tok = __builtin_amdgcn_ds_bpermute(4 * m, tokv);
+                raw[i] = moe::gload<u32x4_t>(static_cast<const uint16_t *>(a.act) + (size_t)tok * K + 8 * kc);
+            }
+            // Unconditional: a chunk past the end re-writes chunk 0 with its
+            // own value, and no load of the batch is left in flight on any path.
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const uint4 v = uint4{raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
+                *reinterpret_cast<uint4 *>(xs + dst[i]) = v;
+                mx[i] = absmax8(v);
+            }
+        } else {
+            f32x4_t f0[SB], f1[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int idx = base + i * kThreads + (int)threadIdx.x;
+                const int ic = idx < nch ? idx : 0;
+                const int m = ic / cpr, kc = ic - m * cpr;
+                row[i] = m;
+                const float *src = static_cast<const float *>(a.act) + (size_t)(row0 + m) * K + 8 * kc;
+                f0[i] = moe::gload<f32x4_t>(src);
+                f1[i] = moe::gload<f32x4_t>(src + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const float a0 = fmaxf(fmaxf(fabsf(f0[i][0]), fabsf(f0[i][1])), fmaxf(fabsf(f0[i][2]), fabsf(f0[i][3])));
+                const float a1 = fmaxf(fmaxf(fabsf(f1[i][0]), fabsf(f1[i][1])), fmaxf(fabsf(f1[i][2]), fabsf(f1[i][3])));
+                mx[i] = fmaxf(a0, a1);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(mx[i]));
+    }
+}
+
+// Gate+up: the staged bf16 rows -> fp16 in place, row m scaled by 2^-e(m).
+// Down: rows of h read again and written to LDS as fp16, scaled the same way.
+template <bool GATED>
+__device__ __forceinline__ void rows_to_f16(const DecArgs &a, int row0, int pr, uint16_t *xs,
+                                            const uint32_t *rmax) {
+    const int K = a.K, cpr = K >> 3;
+    const int nch = pr * cpr;
     if constexpr (GATED) {
-        const int units = (16 * rowb) >> 4;  // per matrix
-        const uint8_t *ga = sA + (size_t)n0 * rowb, *gb = sB + (size_t)n0 * rowb;
-        for (int u = threadIdx.x; u < 2 * units; u += kThreads) {
-            const uint8_t *src = u < units ? ga + 16 * u : gb + 16 * (u - units);
-            *reinterpret_cast<uint4 *>(sl + 16 * u) = moe::gload<uint4>(src);
+        for (int idx = threadIdx.x; idx < nch; idx += kThreads) {
+            const int m = idx / cpr, kc = idx - m * cpr;
+            const float f = exp2i(-row_exp(rmax[m]));
+            uint4 *p = reinterpret_cast<uint4 *>(xs + m * a.ldx + 8 * kc);
+            const uint4 v = *p;
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+            f16x8_t h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[2 * i] = (_Float16)(bf16_lo(u[i]) * f);
+                h[2 * i + 1] = (_Float16)(bf16_hi(u[i]) * f);
+            }
+            *reinterpret_cast<f16x8_t *>(p) = h;
         }
     } else {
-        const int units = (32 * rowb) >> 4;
-        const uint8_t *ga = sA + (size_t)n0 * rowb;
-        for (int u = threadIdx.x; u < units; u += kThreads)
-            *reinterpret_cast<uint4 *>(sl + 16 * u) = moe::gload<uint4>(ga + 16 * u);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// VALU path (one routed row)
-// ---------------------------------------------------------------------------
-
-// acc += s_lo * sum_{e<16} w_e a_e + s_hi * sum_{e>=16} w_e a_e over one chunk.
-__device__ __forceinline__ float chunk_fma(const uint4 &w, uint32_t sc, const float (&a)[32], float acc) {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float p[2] = {0.f, 0.f};
+        constexpr int SB = 4;
+        for (int base = 0; base < nch; base += kThreads * SB) {
+            int dst[SB];
+            float f[SB];
+            f32x4_t f0[SB], f1[SB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float s0 = 0.f, s1 = 0.f;
+            for (int i = 0; i < SB; ++i) {
+                const int idx = base + i * kThreads + (int)threadIdx.x;
+                const int ic = idx < nch ? idx : 0;
+                const int m = ic / cpr, kc = ic - m * cpr;
+                dst[i] = m * a.ldx + 8 * kc;
+                f[i] = exp2i(-row_exp(rmax[m]));
+                const float *src = static_cast<const float *>(a.act) + (size_t)(row0 + m) * K + 8 * kc;
+                f0[i] = moe::gload<f32x4_t>(src);
+                f1[i] = moe::gload<f32x4_t>(src + 4);
+            }
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const uint32_t v = ww[2 * h + d];
-            const f32x2_t e0 = e2m1x2_f32<0>(v), e1 = e2m1x2_f32<1>(v), e2 = e2m1x2_f32<2>(v),
-                          e3 = e2m1x2_f32<3>(v);
-            const int o = 16 * h + 8 * d;
-            s0 = fmaf(e0.x, a[o + 0], s0);
-            s1 = fmaf(e0.y, a[o + 1], s1);
-            s0 = fmaf(e1.x, a[o + 2], s0);
-            s1 = fmaf(e1.y, a[o + 3], s1);
-            s0 = fmaf(e2.x, a[o + 4], s0);
-            s1 = fmaf(e2.y, a[o + 5], s1);
-            s0 = fmaf(e3.x, a[o + 6], s0);
-            s1 = fmaf(e3.y, a[o + 7], s1);
+            for (int i = 0; i < SB; ++i) {
+                f16x8_t h;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h[j] = (_Float16)(f0[i][j] * f[i]);
+                    h[4 + j] = (_Float16)(f1[i][j] * f[i]);
+                }
+                *reinterpret_cast<f16x8_t *>(xs + dst[i]) = h;  // unconditional, as above
+            }
         }
-        p[h] = s0 + s1;
     }
-    return fmaf(moe::e4m3_f32<1>(sc), p[1], fmaf(moe::e4m3_f32<0>(sc), p[0], acc));
 }
 
-// The one activation row -> LDS as bf16 (h is rounded to bf16 here).
-template <bool GATED>
-__device__ __forceinline__ void stage_row(const DecArgs &a, int pos, uint16_t *xs) {
-    const int K = a.K;
+// One pass: rows [row0, row0 + pr) of the expert against units
+// [u_first, u_first + nu) of its weights.
+template <bool GATED, int D>
+__device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
+                                         const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
+                                         const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
+    static_assert(D % kGroup == 0, "ring depth");
+    const int K = a.K, N = a.N, ldx = a.ldx;
+    const int rowbytes = K >> 1, sbytes = K >> 4;
+    const int nseg = (rowbytes + kSegBytes - 1) / kSegBytes;
+    const int total = nu * nseg;
+    const int lane = threadIdx.x & 63, w = moe::wave_id();
+    const int n = lane & 15, q = lane >> 4;
+    const int rho = n >> 2, c = n & 3;
+    const int choff = 64 * q + 16 * c;  // this lane's chunk within a row segment
+    // Scale-load role: step s4 of the group, row r8 of the wave, half hh of the 32-byte slice.
+    const int s4 = lane >> 4, r8 = (lane >> 1) & 7, hh = lane & 1;
+
+    uint8_t *sc_lds = lds + w * kScaleLds;
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kWaves * kScaleLds);
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds + kHdrLds);
+
+    // Row bases (bytes) of this lane's two weight rows and its scale row, in unit 0.
+    const uint8_t *wb0, *wb1, *sbase;
+    size_t ustride, sustride;  // advance per unit
     if constexpr (GATED) {
-        const uint16_t *src =
-            static_cast<const uint16_t *>(a.act) + (size_t)moe::gload<int32_t>(a.sorted_tok + pos) * K;
-        for (int u = threadIdx.x; u < (K >> 3); u += kThreads)
-            reinterpret_cast<uint4 *>(xs)[u] = moe::gload<uint4>(src + 8 * u);
+        wb0 = pA + (size_t)(4 * w + rho) * rowbytes;
+        wb1 = pB + (size_t)(4 * w + rho) * rowbytes;
+        sbase = (r8 < 4 ? sA : sB) + (size_t)(4 * w + (r8 & 3)) * sbytes;
+        ustride = (size_t)16 * rowbytes;
+        sustride = (size_t)16 * sbytes;
     } else {
-        const float *src = static_cast<const float *>(a.act) + (size_t)pos * K;
-        for (int u = threadIdx.x; u < (K >> 2); u += kThreads) {
-            const float4 f = moe::gload<float4>(src + 4 * u);
-            uint2 v;
-            v.x = (uint32_t)moe::f32_to_bf16_rne(f.x) | ((uint32_t)moe::f32_to_bf16_rne(f.y) << 16);
-            v.y = (uint32_t)moe::f32_to_bf16_rne(f.z) | ((uint32_t)moe::f32_to_bf16_rne(f.w) << 16);
-            reinterpret_cast<uint2 *>(xs)[u] = v;
-        }
+        wb0 = pA + (size_t)(8 * w + rho) * rowbytes;
+        wb1 = wb0 + (size_t)4 * rowbytes;
+        sbase = sA + (size_t)(8 * w + r8) * sbytes;
+        ustride = (size_t)32 * rowbytes;
+        sustride = (size_t)32 * sbytes;
     }
-}
 
-template <bool GATED>
-__device__ __forceinline__ void valu_one_row(const DecArgs &a, int pos, int n0, const uint8_t *p0,
-                                             const uint8_t *p1, float s2A, float s2B, const uint8_t *sl,
-                                             const uint16_t *xs) {
-    constexpr int D = kDepth;
-    const int K = a.K, N = a.N;
-    const int g = threadIdx.x >> 4, j = threadIdx.x & 15;
-    const int Kc = K >> 5;
-    const int nch = (Kc + 15) >> 4;  // uniform trip count
-    const int rowb = K >> 4;
-    const uint8_t *sl0 = sl + g * rowb, *sl1 = sl + (g + 16) * rowb;
-
-    uint4 w0[D], w1[D];
-    bool ok[D];
-    auto load = [&](int d, int i) {
-        const int cr = j + 16 * i;
-        ok[d] = i < nch && cr < Kc;
-        const int c = ok[d] ? cr : 0;  // past the end: load chunk 0, its products are dropped
-        w0[d] = moe::gload<uint4>(p0 + (size_t)c * 16);
-        w1[d] = moe::gload<uint4>(p1 + (size_t)c * 16);
+    u32x4_t w0[D], w1[D], sv[D / kGroup];
+    int ssh[D / kGroup];  // dword shift of a scale slice loaded from a clamped address
+    int lu = 0, li = 0;   // stream position of the next load (unit, segment)
+    auto load = [&](int d) {
+        if (d % kGroup == 0) {
+            // Scale slice of step (lu, li) + s4 for row r8 (16 bytes, half hh).
+            int l = li + s4, u = lu;
+#pragma unroll
+            for (int i = 0; i < kGroup - 1; ++i) {
+                const bool wrap = l >= nseg;
+                l = wrap ? l - nseg : l;
+                u = wrap ? u + 1 : u;
+            }
+            const bool real = u < nu;
+            u = real ? u : nu - 1;
+            l = real ? l : nseg - 1;
+            const int want = 32 * l + 16 * hh;
+            const int got = min(want, sbytes - 16);
+            ssh[d / kGroup] = (want - got) >> 2;
+            sv[d / kGroup] = moe::gload<u32x4_t>(sbase + (size_t)(u_first + u) * sustride + got);
+        }
+        const bool real = lu < nu;  // past the end: the last real step again
+        const int unit = u_first + (real ? lu : nu - 1);
+        const int off = min(kSegBytes * (real ? li : nseg - 1) + choff, rowbytes - 16);
+        w0[d] = moe::gload<u32x4_t>(wb0 + (size_t)unit * ustride + off);
+        w1[d] = moe::gload<u32x4_t>(wb1 + (size_t)unit * ustride + off);
+        if (++li == nseg) {
+            li = 0;
+            ++lu;
+        }
     };
+
+    if (threadIdx.x < 16) rmax[threadIdx.x] = 0u;
+    int tokv = 0;  // gate+up: token of row (lane & 15) of the pass
+    if constexpr (GATED) tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    __syncthreads();  // rmax cleared
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load(d, d);
+        load(d);
         __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
     }
-    __syncthreads();  // scales and the activation row are in LDS
+    stage_rows<GATED>(a, row0, pr, tokv, xs, rmax);
+    __syncthreads();  // staged rows and their maxima are complete
+    rows_to_f16<GATED>(a, row0, pr, xs, rmax);
+    __syncthreads();  // fp16 rows are visible
 
-    float acc0 = 0.f, acc1 = 0.f;
+    const int TG = (pr + 3) >> 2;
+    const int tA = n >> 2, cA = n & 3;  // A-operand role: token tA of each group, quarter cA
+    int arow[kMaxTG];
+    float oscale[kMaxTG];  // undoes the row scaling of this lane's output token
+#pragma unroll
+    for (int tg = 0; tg < kMaxTG; ++tg) {
+        const int t = 4 * tg + tA;
+        arow[tg] = (t < pr ? t : 0) * ldx;  // rows past the pass read row 0: dropped outputs
+        const int to = 4 * tg + q;
+        oscale[tg] = exp2i(row_exp(rmax[to < pr ? to : 0]));
+    }
+    const int sread0 = 32 * rho + 8 * q + 2 * c;  // this lane's scale bytes in a step's slice (group 0)
+
+    f32x4_t acc0[kMaxTG], acc1[kMaxTG];
+#pragma unroll
+    for (int tg = 0; tg < kMaxTG; ++tg) acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    int cu = 0, ci = 0;  // stream position being computed
     // The trip count is padded to a multiple of the ring and every step refills
-    // its slot, so the loop body has no branch around a load; padded and
-    // out-of-range chunks add nothing.
-    for (int base = 0; base < nch; base += D) {
+    // its slot, so the loop body has no branch around a load.
+    for (int base = 0; base < total; base += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int i = base + d;
-            const int c = ok[d] ? j + 16 * i : 0;
-            const uint4 *xc = reinterpret_cast<const uint4 *>(xs) + (size_t)c * 4;
-            float av[32];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 u = xc[v];
-                const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    av[8 * v + 2 * k] = __uint_as_float(uu[k] << 16);
-                    av[8 * v + 2 * k + 1] = __uint_as_float(uu[k] & 0xffff0000u);
-                }
+            if (d % kGroup == 0) {
+                // This group's scale slices -> LDS (undoing a clamped load's shift).
+                const u32x4_t v = sv[d / kGroup];
+                const int s = ssh[d / kGroup];
+                u32x4_t r;
+                r[0] = s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3]));
+                r[1] = s == 0 ? v[1] : (s == 1 ? v[2] : v[3]);
+                r[2] = s == 0 ? v[2] : v[3];
+                r[3] = v[3];
+                *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
             }
-            const uint32_t s0 = *reinterpret_cast<const uint16_t *>(sl0 + 2 * c);
-            const uint32_t s1 = *reinterpret_cast<const uint16_t *>(sl1 + 2 * c);
-            const float n0v = chunk_fma(w0[d], s0, av, acc0);
-            const float n1v = chunk_fma(w1[d], s1, av, acc1);
-            acc0 = ok[d] ? n0v : acc0;
-            acc1 = ok[d] ? n1v : acc1;
-            __builtin_amdgcn_sched_barrier(0);
-            load(d, i + D);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    acc0 = moe::group_sum<16>(acc0);
-    acc1 = moe::group_sum<16>(acc1);
-    if (j == 0) {
-        if constexpr (GATED) {
-            a.out[(size_t)pos * N + n0 + g] = moe::silu_f32(acc0 * s2A) * (acc1 * s2B);
-        } else {
-            a.out[(size_t)pos * N + n0 + g] = acc0 * s2A;
-            a.out[(size_t)pos * N + n0 + g + 16] = acc1 * s2A;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// MFMA path (two or more routed rows)
-// ---------------------------------------------------------------------------
-
-// 8 E2M1 codes (one 32-bit word: k .. k+7) times the block scale, as bf16.
-// The f32 products are exact (at most 6 significant bits), so is their bf16 form.
-__device__ __forceinline__ bf16x8_t decode_b(uint32_t w, float s) {
-    const f32x2_t v0 = e2m1x2_f32<0>(w), v1 = e2m1x2_f32<1>(w), v2 = e2m1x2_f32<2>(w), v3 = e2m1x2_f32<3>(w);
-    const bf16x2v_t r0 = __builtin_convertvector((f32x2_t){v0.x * s, v0.y * s}, bf16x2v_t);
-    const bf16x2v_t r1 = __builtin_convertvector((f32x2_t){v1.x * s, v1.y * s}, bf16x2v_t);
-    const bf16x2v_t r2 = __builtin_convertvector((f32x2_t){v2.x * s, v2.y * s}, bf16x2v_t);
-    const bf16x2v_t r3 = __builtin_convertvector((f32x2_t){v3.x * s, v3.y * s}, bf16x2v_t);
-    bf16x8_t r;
-    r[0] = r0.x;
-    r[1] = r0.y;
-    r[2] = r1.x;
-    r[3] = r1.y;
-    r[4] = r2.x;
-    r[5] = r2.y;
-    r[6] = r3.x;
-    r[7] = r3.y;
-    return r;
-}
-
-__device__ __forceinline__ bf16x8_t f32x8_to_bf16(const uint4 &x0, const uint4 &x1) {
-    const bf16x2v_t r0 = __builtin_convertvector((f32x2_t){__uint_as_float(x0.x), __uint_as_float(x0.y)}, bf16x2v_t);
-    const bf16x2v_t r1 = __builtin_convertvector((f32x2_t){__uint_as_float(x0.z), __uint_as_float(x0.w)}, bf16x2v_t);
-    const bf16x2v_t r2 = __builtin_convertvector((f32x2_t){__uint_as_float(x1.x), __uint_as_float(x1.y)}, bf16x2v_t);
-    const bf16x2v_t r3 = __builtin_convertvector((f32x2_t){__uint_as_float(x1.z), __uint_as_float(x1.w)}, bf16x2v_t);
-    bf16x8_t r;
-    r[0] = r0.x;
-    r[1] = r0.y;
-    r[2] = r1.x;
-    r[3] = r1.y;
-    r[4] = r2.x;
-    r[5] = r2.y;
-    r[6] = r3.x;
-    r[7] = r3.y;
-    return r;
-}
-
-template <bool GATED>
-struct KTile {
-    uint4 w0, w1;             // 16-byte chunk of each row of the pair
-    uint4 av[GATED ? 4 : 8];  // activation row r: 32 bf16 (x) or 32 fp32 (h)
-};
-
-template <bool GATED>
-__device__ __forceinline__ void mfma_rows(const DecArgs &a, int lo, int rows, int n0, const uint8_t *p0,
-                                          const uint8_t *p1, float s2A, float s2B, const uint8_t *sl,
-                                          float *red) {
-    const int K = a.K, N = a.N;
-    const int lane = threadIdx.x & 63, w = moe::wave_id();
-    const int r = lane & 15, q = lane >> 4;
-    const int rowb = K >> 4;
-    const uint8_t *sl0 = sl + r * rowb, *sl1 = sl + (r + 16) * rowb;
-    const int c0 = n0 + r;
-    const int c1 = GATED ? n0 + r : n0 + r + 16;
-    const int nkt = (K + kKT - 1) / kKT;
-    const int cnt = w < nkt ? (nkt - 1 - w) / kWaves + 1 : 0;
-    __syncthreads();  // scales are in LDS
-
-    for (int m0 = 0; m0 < rows; m0 += kPassRows) {
-        const int mr = min(kPassRows, rows - m0);
-        // Rows past the pass read the pass's row 0: they only feed dropped outputs.
-        const int mrow = lo + m0 + (r < mr ? r : 0);
-        const void *arow;
-        if constexpr (GATED)
-            arow = static_cast<const uint16_t *>(a.act) + (size_t)moe::gload<int32_t>(a.sorted_tok + mrow) * K;
-        else
-            arow = static_cast<const float *>(a.act) + (size_t)mrow * K;
-
-        KTile<GATED> ring[kRing];
-        bool kin[kRing];
-        int kq_[kRing];
-        auto load = [&](int d, int i) {
-            const int kr = (w + kWaves * min(i, cnt - 1)) * kKT + 32 * q;
-            kin[d] = i < cnt && kr < K;
-            const int kq = kin[d] ? kr : 0;  // padding / past the end: k = 0, scaled by zero below
-            kq_[d] = kq;
-            ring[d].w0 = moe::gload<uint4>(p0 + (kq >> 1));
-            ring[d].w1 = moe::gload<uint4>(p1 + (kq >> 1));
-            constexpr int NV = GATED ? 4 : 8;
+            const int kq = 512 * ci + 128 * q + 32 * c;  // first k of this lane's B chunk
+            const bool kin = cu < nu && kq < K;
+            const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
+            const uint32_t v0 = *reinterpret_cast<const uint16_t *>(sp);
+            const uint32_t v1 = *reinterpret_cast<const uint16_t *>(sp + 128);
+            const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
+            const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, 1.0f, false) : zero2;
+            const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, 1.0f, false) : zero2;
+            const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
+            const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
+            f16x8_t b0[4], b1[4];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                if constexpr (GATED)
-                    ring[d].av[v] = moe::gload<uint4>(static_cast<const uint16_t *>(arow) + kq + 8 * v);
-                else
-                    ring[d].av[v] = moe::gload<uint4>(static_cast<const float *>(arow) + kq + 4 * v);
+            for (int ks = 0; ks < 4; ++ks) {
+                b0[ks] = decode_b(w0[d][ks], ks < 2 ? sl0 : sh0);
+                b1[ks] = decode_b(w1[d][ks], ks < 2 ? sl1 : sh1);
             }
-        };
-
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-        if (cnt > 0) {  // uniform: a wave past the last K-tile only adds zeros below
+            const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
+            const int kac = ka < K ? ka : 0;              // past the end: any finite row data
 #pragma unroll
-            for (int d = 0; d < kRing; ++d) {
-                load(d, d);
-                __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-            }
-            // The trip count is padded to a multiple of the ring and every step
-            // refills its slot (padding tiles have zero scales), so the loop body
-            // has no branch around a load and the waits on the ring stay partial.
-            for (int base = 0; base < cnt; base += kRing) {
-#pragma unroll
-                for (int d = 0; d < kRing; ++d) {
-                    const KTile<GATED> &t = ring[d];
-                    const uint32_t r0 = *reinterpret_cast<const uint16_t *>(sl0 + (kq_[d] >> 4));
-                    const uint32_t r1 = *reinterpret_cast<const uint16_t *>(sl1 + (kq_[d] >> 4));
-                    const uint32_t s0 = kin[d] ? r0 : 0u, s1 = kin[d] ? r1 : 0u;
-                    const float sl_0 = moe::e4m3_f32<0>(s0), sh_0 = moe::e4m3_f32<1>(s0);
-                    const float sl_1 = moe::e4m3_f32<0>(s1), sh_1 = moe::e4m3_f32<1>(s1);
-                    const uint32_t u0[4] = {t.w0.x, t.w0.y, t.w0.z, t.w0.w};
-                    const uint32_t u1[4] = {t.w1.x, t.w1.y, t.w1.z, t.w1.w};
+            for (int tg = 0; tg < kMaxTG; ++tg) {
+                if (tg < TG) {
+                    const uint16_t *ap = xs + arow[tg] + kac;
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        bf16x8_t A;
-                        if constexpr (GATED)
-                            A = moe::bitcast<bf16x8_t>(t.av[ks]);
-                        else
-                            A = f32x8_to_bf16(t.av[2 * ks], t.av[2 * ks + 1]);
-                        const bf16x8_t b0 = decode_b(u0[ks], ks < 2 ? sl_0 : sh_0);
-                        const bf16x8_t b1 = decode_b(u1[ks], ks < 2 ? sl_1 : sh_1);
-                        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b0, acc0, 0, 0, 0);
-                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, b1, acc1, 0, 0, 0);
+                        const f16x8_t A = *reinterpret_cast<const f16x8_t *>(ap + 8 * ks);
+                        acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b0[ks], acc0[tg], 0, 0, 0);
+                        acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b1[ks], acc1[tg], 0, 0, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    load(d, base + d + kRing);
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
-
-        // Sum the four waves' partial tiles: red[((w*2 + mat)*4 + i)*64 + lane].
-        __syncthreads();  // the previous pass's readers are done
+            if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
+                const int unit = u_first + cu;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            red[((w * 2 + 0) * 4 + i) * 64 + lane] = acc0[i];
-            red[((w * 2 + 1) * 4 + i) * 64 + lane] = acc1[i];
-        }
-        __syncthreads();
-        // Wave w finishes row i = w of each lane's four: row 4q + w of the tile.
-        {
-            const int i = w;
-            float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                v0 += red[((ww * 2 + 0) * 4 + i) * 64 + lane];
-                v1 += red[((ww * 2 + 1) * 4 + i) * 64 + lane];
-            }
-            const int m = m0 + 4 * q + i;
-            if (m < rows) {
-                float *o = a.out + (size_t)(lo + m) * N;
-                if constexpr (GATED) {
-                    o[c0] = moe::silu_f32(v0 * s2A) * (v1 * s2B);
-                } else {
-                    o[c0] = v0 * s2A;
-                    o[c1] = v1 * s2A;
+                for (int tg = 0; tg < kMaxTG; ++tg) {
+                    if (tg < TG) {
+                        // Lane (n, t) holds rows 4t..4t+3 of column n; the kept
+                        // block is row 4t + (n & 3).  Sum the quarters of a quad.
+                        const float g0 = moe::group_sum<4>(pick(acc0[tg], c)) * oscale[tg];
+                        const float g1 = moe::group_sum<4>(pick(acc1[tg], c)) * oscale[tg];
+                        const int tl = 4 * tg + q;
+                        if (c == 0 && tl < pr) {
+                            float *o = a.out + (size_t)(row0 + tl) * N;
+                            if constexpr (GATED) {
+                                o[16 * unit + 4 * w + rho] = moe::silu_f32(g0 * s2A) * (g1 * s2B);
+                            } else {
+                                o[32 * unit + 8 * w + rho] = g0 * s2A;
+                                o[32 * unit + 8 * w + 4 + rho] = g1 * s2A;
+                            }
+                        }
+                        acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
             }
+            if (++ci == nseg) {
+                ci = 0;
+                ++cu;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load(d);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
-    // LDS: [the unit's scales: 32 x K/16 bytes][activation row (VALU) | partial tiles (MFMA)]
     extern __shared__ uint4 lds4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
 
     const int e = a.active[blockIdx.y];  // -1 past the active count
     if (e < 0) return;
+    const int u_first = blockIdx.x * a.G;
+    const int nu = min(a.G, a.units - u_first);
+    if (nu <= 0) return;
     const int lo = a.offsets[e], rows = a.offsets[e + 1] - lo;
-    const int K = a.K;
-    const int n0 = blockIdx.x * (GATED ? kUnitRows / 2 : kUnitRows);
+    constexpr int ucols = GATED ? 16 : 32;
     const uint8_t *pA = a.pa[e];
     const uint8_t *pB = GATED ? a.pb[e] : pA;
     if (pA == nullptr || pB == nullptr) {  // absent expert: its rows are zero
-        const int ncols = GATED ? kUnitRows / 2 : kUnitRows;
+        const int ncols = nu * ucols, n0 = u_first * ucols;
         for (int i = threadIdx.x; i < rows * ncols; i += kThreads) {
             const int m = i / ncols;
             a.out[(size_t)(lo + m) * a.N + n0 + (i - m * ncols)] = 0.f;
@@ -403,28 +450,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     const uint8_t *sB = GATED ? a.sb[e] : sA;
     const float s2A = a.s2a[e];
     const float s2B = GATED ? a.s2b[e] : s2A;
-    const size_t rb = (size_t)(K >> 1);
-    uint8_t *sl = lds;
-    uint8_t *rest = lds + 2 * (size_t)K;  // after 32 rows x K/16 bytes of scales
-    stage_scales<GATED>(K, n0, sA, sB, sl);
-
-    if (rows == 1) {
-        const int g = threadIdx.x >> 4;
-        const uint8_t *p0 = pA + (size_t)(n0 + g) * rb;
-        const uint8_t *p1 = GATED ? pB + (size_t)(n0 + g) * rb : pA + (size_t)(n0 + g + 16) * rb;
-        stage_row<GATED>(a, lo, reinterpret_cast<uint16_t *>(rest));
-        valu_one_row<GATED>(a, lo, n0, p0, p1, s2A, s2B, sl, reinterpret_cast<const uint16_t *>(rest));
-    } else {
-        const int r = threadIdx.x & 15;
-        const uint8_t *p0 = pA + (size_t)(n0 + r) * rb;
-        const uint8_t *p1 = GATED ? pB + (size_t)(n0 + r) * rb : pA + (size_t)(n0 + r + 16) * rb;
-        mfma_rows<GATED>(a, lo, rows, n0, p0, p1, s2A, s2B, sl, reinterpret_cast<float *>(rest));
+    for (int m0 = 0; m0 < rows; m0 += a.pass_rows) {
+        if (m0 > 0) __syncthreads();  // the previous pass's readers of LDS are done
+        run_pass<GATED, kDepth>(a, lo + m0, min(a.pass_rows, rows - m0), u_first, nu, pA, sA, pB, sB, s2A,
+                                s2B, lds);
     }
 }
 
 }  // namespace
 
 // Launch the row-major grouped projection (used by the two C-ABI entry points).
+// Shapes: N % 64 == 0, K % 64 == 0 and K >= 256 (checked by the callers).
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const moe_nvfp4_experts &A, const moe_nvfp4_experts *B,
                           float *out, int N, int K, int P, int E, hipStream_t stream) {
@@ -442,13 +478,25 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.out = out;
     a.N = N;
     a.K = K;
-    const int cols = gated ? kUnitRows / 2 : kUnitRows;
+    const int ucols = gated ? 16 : 32;
+    a.units = (N + ucols - 1) / ucols;
+    // Units per block: about 32 blocks along N per expert, at most 4 units each.
+    int G = a.units / 32;
+    G = G < 1 ? 1 : (G > 4 ? 4 : G);
+    a.G = G;
+    // Staged row stride: 2K bytes padded to 16 mod 256, so the 16 lanes of an
+    // A-operand read (4 rows x 4 quarters, 64 bytes apart) hit distinct banks.
+    const int pad_bytes = ((16 - (2 * K) % 256) + 256) % 256;
+    a.ldx = K + pad_bytes / 2;
+    const size_t row_lds = (size_t)a.ldx * 2;
+    int pr = (int)(kLdsBudget / row_lds);
+    if (pr < 1) return MOE_NVFP4_ELIMIT;
+    if (pr > 4 * kMaxTG) pr = 4 * kMaxTG;
+    if (pr > P) pr = P;
+    a.pass_rows = pr;
+    const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
     const int cap = E < P ? E : P;
-    dim3 grid((unsigned)((N + cols - 1) / cols), (unsigned)cap);
-    size_t tail = (size_t)kRedBytes;                  // MFMA partial tiles
-    if ((size_t)K * 2 > tail) tail = (size_t)K * 2;   // VALU activation row (bf16)
-    const size_t lds = (size_t)K * 2 + tail;          // + the unit's scales
-    if (lds > 160 * 1024) return MOE_NVFP4_ELIMIT;
+    dim3 grid((unsigned)((a.units + G - 1) / G), (unsigned)cap);
     if (gated)
         hipLaunchKernelGGL(k_decode_row<true>, grid, dim3(kThreads), lds, stream, a);
     else

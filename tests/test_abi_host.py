@@ -51,7 +51,9 @@ def test_gate_up_rejects():
     assert call(g=_ex(null=True)) == ENULL
     assert call(g=_ex(0), u=_ex(1)) == ELAYOUT
     assert call(g=_ex(7), u=_ex(7)) == ELAYOUT
-    assert call(H=48) == ESHAPE                         # row-major needs H % 32 == 0
+    assert call(H=48) == ESHAPE                         # H % 64 != 0
+    assert call(H=96) == ESHAPE                         # H % 64 != 0
+    assert call(H=192) == ESHAPE                        # row-major needs H >= 256
     assert call(I=528, g=_ex(1), u=_ex(1)) == ESHAPE    # K-major needs I % 64 == 0
     assert call(k=5) == ESHAPE
     assert call(H=1 << 17) == ELIMIT
