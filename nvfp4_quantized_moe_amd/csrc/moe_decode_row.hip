@@ -72,6 +72,7 @@ struct DecArgs {
     const int32_t *sorted_tok;  // gate+up only
     const int32_t *offsets;
     const int32_t *active;
+    const int32_t *nactive;
     const uint8_t *const *pa;   // gate (or down)
     const uint8_t *const *sa;
     const float *s2a;
@@ -84,6 +85,7 @@ struct DecArgs {
     int units;                  // units along N
     int pass_rows;              // activation rows staged per pass
     int ldx;                    // staged row stride, fp16 elements
+    int extra;                  // block rows for passes beyond each expert's first
 };
 
 // 8 E2M1 codes (one 32-bit word: k .. k+7) times the block scale, as fp16.
@@ -424,25 +426,60 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     }
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
-    extern __shared__ uint4 lds4[];
-    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+// Block-wide exclusive prefix sum of the further passes (beyond the first)
+// of the active slots: pre[s] for s < n, pre[n] = total.  n <= 1024.
+__device__ __forceinline__ void extra_pass_prefix(const DecArgs &a, int n, int *pre) {
+    __shared__ int wsum[kWaves];
+    const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * t + i;
+        int r = 0;
+        if (sl < n) {
+            const int e = a.active[sl];
+            r = a.offsets[e + 1] - a.offsets[e];
+        }
+        c[i] = r > 0 ? (r - 1) / a.pass_rows : 0;
+        sum += c[i];
+    }
+    int incl = sum;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += wsum[i];
+    int run = base + incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * t + i;
+        if (sl < n) pre[sl] = run;
+        run += c[i];
+    }
+    if (t == kThreads - 1) pre[n] = run;  // the total
+    __syncthreads();
+}
 
-    const int e = a.active[blockIdx.y];  // -1 past the active count
+template <bool GATED>
+__device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, uint8_t *lds) {
+    const int e = a.active[slot];  // -1 past the active count
     if (e < 0) return;
-    const int u_first = blockIdx.x * a.G;
-    const int nu = min(a.G, a.units - u_first);
-    if (nu <= 0) return;
     const int lo = a.offsets[e], rows = a.offsets[e + 1] - lo;
+    const int m0 = pass * a.pass_rows;
+    if (m0 >= rows) return;
+    const int pr = min(a.pass_rows, rows - m0);
     constexpr int ucols = GATED ? 16 : 32;
     const uint8_t *pA = a.pa[e];
     const uint8_t *pB = GATED ? a.pb[e] : pA;
     if (pA == nullptr || pB == nullptr) {  // absent expert: its rows are zero
         const int ncols = nu * ucols, n0 = u_first * ucols;
-        for (int i = threadIdx.x; i < rows * ncols; i += kThreads) {
+        for (int i = threadIdx.x; i < pr * ncols; i += kThreads) {
             const int m = i / ncols;
-            a.out[(size_t)(lo + m) * a.N + n0 + (i - m * ncols)] = 0.f;
+            a.out[(size_t)(lo + m0 + m) * a.N + n0 + (i - m * ncols)] = 0.f;
         }
         return;
     }
@@ -450,10 +487,44 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     const uint8_t *sB = GATED ? a.sb[e] : sA;
     const float s2A = a.s2a[e];
     const float s2B = GATED ? a.s2b[e] : s2A;
-    for (int m0 = 0; m0 < rows; m0 += a.pass_rows) {
-        if (m0 > 0) __syncthreads();  // the previous pass's readers of LDS are done
-        run_pass<GATED, kDepth>(a, lo + m0, min(a.pass_rows, rows - m0), u_first, nu, pA, sA, pB, sB, s2A,
-                                s2B, lds);
+    run_pass<GATED, kDepth>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+}
+
+// Block (x, y): units [x G, x G + G) of
+//   y >= extra: the first pass (rows 0 .. pass_rows) of active slot y - extra;
+//   y <  extra: further passes number y, y + extra, ... in slot order, so an
+//               expert with many routed rows is spread over many blocks of
+//               about the same length as the rest.
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
+    extern __shared__ uint4 lds4[];
+    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+    const int u_first = blockIdx.x * a.G;
+    const int nu = min(a.G, a.units - u_first);
+    if (nu <= 0) return;
+    const int y = blockIdx.y;
+    if (y >= a.extra) {
+        do_pass<GATED>(a, y - a.extra, 0, u_first, nu, lds);
+        return;
+    }
+    int *pre = reinterpret_cast<int *>(lds);  // [n + 1], in the scale areas (free until a pass starts)
+    const int n = *a.nactive;
+    extra_pass_prefix(a, n, pre);
+    const int total = pre[n];
+    for (int g = y; g < total; g += a.extra) {
+        int lo = 0, hi = n - 1;  // last slot with pre[slot] <= g
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= g) lo = mid;
+            else hi = mid - 1;
+        }
+        const int slot = lo, pass = 1 + g - pre[lo];
+        __syncthreads();  // every thread has read pre[] before a pass reuses the area
+        do_pass<GATED>(a, slot, pass, u_first, nu, lds);
+        if (g + a.extra < total) {
+            __syncthreads();  // the pass's readers of LDS are done
+            extra_pass_prefix(a, n, pre);
+        }
     }
 }
 
@@ -462,13 +533,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
 // Launch the row-major grouped projection (used by the two C-ABI entry points).
 // Shapes: N % 64 == 0, K % 64 == 0 and K >= 256 (checked by the callers).
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
-                          const int32_t *active, const moe_nvfp4_experts &A, const moe_nvfp4_experts *B,
-                          float *out, int N, int K, int P, int E, hipStream_t stream) {
+                          const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
+                          const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
+                          hipStream_t stream) {
     DecArgs a;
     a.act = act;
     a.sorted_tok = sorted_tok;
     a.offsets = offsets;
     a.active = active;
+    a.nactive = nactive;
     a.pa = A.packed;
     a.sa = A.scale;
     a.s2a = A.scale2;
@@ -496,7 +569,12 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.pass_rows = pr;
     const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
     const int cap = E < P ? E : P;
-    dim3 grid((unsigned)((a.units + G - 1) / G), (unsigned)cap);
+    // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
+    // the grid's y extent is kept within its limit by striding over them.
+    int extra = (P - 1) / pr;
+    if (extra > 64) extra = 64;
+    a.extra = extra;
+    dim3 grid((unsigned)((a.units + G - 1) / G), (unsigned)(cap + extra));
     if (gated)
         hipLaunchKernelGGL(k_decode_row<true>, grid, dim3(kThreads), lds, stream, a);
     else

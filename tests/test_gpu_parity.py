@@ -235,9 +235,10 @@ def test_deterministic_and_power_of_two_scaling(cfg):
 
 
 def test_many_rows_one_expert_passes():
-    """One expert takes every token (row-major passes of 8, 4, 2, 1 rows)."""
+    """One expert takes every token: one pass, several passes on their own
+    block rows, and (T=1100) more further passes than block rows for them."""
     say("many rows one expert")
-    for T in (1, 2, 3, 7, 8, 9, 23, 40):
+    for T in (1, 2, 3, 7, 8, 9, 23, 40, 1100):
         shape = synth.MoeShape(f"one_{T}", T, 512, 256, 2, 1, "uniform", False)
         ids = np.zeros((T, 1), dtype=np.int32)
         _full_check(Case(14, shape, ids=ids, weights=np.ones((T, 1), np.float32)), f"one expert T={T}")
