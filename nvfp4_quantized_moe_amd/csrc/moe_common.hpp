@@ -124,6 +124,19 @@ inline bool experts_null(const moe_nvfp4_experts &w) {
     return w.packed == nullptr || w.scale == nullptr || w.scale2 == nullptr;
 }
 
+// Compute units of the current device (cached per device).
+inline int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 inline int launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MOE_NVFP4_OK : (int)e;

@@ -63,9 +63,15 @@ constexpr int kSegBytes = 256;     // bytes of one weight row per step (512 k)
 constexpr int kMaxTG = 4;          // token groups of 4 per pass (16 rows)
 constexpr int kLdsBudget = 72 * 1024;  // staged activation rows per block (two blocks per CU)
 constexpr int kScaleLds = 1024;        // per wave: 4 steps x 8 rows x 32 bytes
-constexpr int kHdrLds = kWaves * kScaleLds + 64;  // scale areas + per-row maxima
+constexpr int kPreLds = 4 * (MOE_NVFP4_MAX_EXPERTS + 4);  // per-slot prefix sums of passes
+constexpr int kRmaxOff = kWaves * kScaleLds;                    // per-row maxima (16 x u32)
+constexpr int kPreOff = kRmaxOff + 64;
+constexpr int kHdrLds = kPreOff + kPreLds;  // scale areas + row maxima + pass prefix; then the rows
 
 using moe::u32x4_t;
+// sched_barrier mask: ALU, VALU, SALU, MFMA, LDS and transcendental
+// instructions may be scheduled across; global memory instructions may not.
+constexpr int kMoveAcrossLoads = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0400;
 
 struct DecArgs {
     const void *act;            // gate+up: bf16 x [T, K]; down: fp32 h [P, K]
@@ -261,7 +267,7 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     const int s4 = lane >> 4, r8 = (lane >> 1) & 7, hh = lane & 1;
 
     uint8_t *sc_lds = lds + w * kScaleLds;
-    uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kWaves * kScaleLds);
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kRmaxOff);
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds + kHdrLds);
 
     // Row bases (bytes) of this lane's two weight rows and its scale row, in unit 0.
@@ -362,6 +368,13 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
                 r[3] = v[3];
                 *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
             }
+            // A fragments of token group 0 (always present), read first so the
+            // LDS latency hides behind the decode.
+            const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
+            const int kac = ka < K ? ka : 0;              // past the end: any finite row data
+            f16x8_t a0[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + arow[0] + kac + 8 * ks);
             const int kq = 512 * ci + 128 * q + 32 * c;  // first k of this lane's B chunk
             const bool kin = cu < nu && kq < K;
             const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
@@ -378,10 +391,13 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
                 b0[ks] = decode_b(w0[d][ks], ks < 2 ? sl0 : sh0);
                 b1[ks] = decode_b(w1[d][ks], ks < 2 ? sl1 : sh1);
             }
-            const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
-            const int kac = ka < K ? ka : 0;              // past the end: any finite row data
 #pragma unroll
-            for (int tg = 0; tg < kMaxTG; ++tg) {
+            for (int ks = 0; ks < 4; ++ks) {
+                acc0[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0[0], 0, 0, 0);
+                acc1[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1[0], 0, 0, 0);
+            }
+#pragma unroll
+            for (int tg = 1; tg < kMaxTG; ++tg) {
                 if (tg < TG) {
                     const uint16_t *ap = xs + arow[tg] + kac;
 #pragma unroll
@@ -419,16 +435,24 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
                 ci = 0;
                 ++cu;
             }
-            __builtin_amdgcn_sched_barrier(0);
+            // Loads keep their order; arithmetic and LDS work may move across.
+            __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
             load(d);
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
         }
     }
 }
 
-// Block-wide exclusive prefix sum of the further passes (beyond the first)
-// of the active slots: pre[s] for s < n, pre[n] = total.  n <= 1024.
-__device__ __forceinline__ void extra_pass_prefix(const DecArgs &a, int n, int *pre) {
+// Passes of an expert with r routed rows: all of them, or those beyond the first.
+template <bool FURTHER>
+__device__ __forceinline__ int passes_of(int r, int pr) {
+    return r <= 0 ? 0 : (FURTHER ? (r - 1) / pr : (r + pr - 1) / pr);
+}
+
+// Block-wide exclusive prefix sum over the active slots of passes_of<FURTHER>:
+// pre[s] for s < n, pre[n] = total.  n <= 1024.
+template <bool FURTHER>
+__device__ __forceinline__ void pass_prefix(const DecArgs &a, int n, int *pre) {
     __shared__ int wsum[kWaves];
     const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
     int c[4], sum = 0;
@@ -440,7 +464,7 @@ __device__ __forceinline__ void extra_pass_prefix(const DecArgs &a, int n, int *
             const int e = a.active[sl];
             r = a.offsets[e + 1] - a.offsets[e];
         }
-        c[i] = r > 0 ? (r - 1) / a.pass_rows : 0;
+        c[i] = passes_of<FURTHER>(r, a.pass_rows);
         sum += c[i];
     }
     int incl = sum;  // inclusive scan over the wave
@@ -462,6 +486,17 @@ __device__ __forceinline__ void extra_pass_prefix(const DecArgs &a, int n, int *
     }
     if (t == kThreads - 1) pre[n] = run;  // the total
     __syncthreads();
+}
+
+// Last slot s < n with pre[s] <= g (pre non-decreasing, pre[0] = 0 <= g).
+__device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= g) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 template <bool GATED>
@@ -490,7 +525,7 @@ __device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, in
     run_pass<GATED, kDepth>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
 }
 
-// Block (x, y): units [x G, x G + G) of
+// Grid mode (small launches).  Block (x, y): units [x G, x G + G) of
 //   y >= extra: the first pass (rows 0 .. pass_rows) of active slot y - extra;
 //   y <  extra: further passes number y, y + extra, ... in slot order, so an
 //               expert with many routed rows is spread over many blocks of
@@ -507,24 +542,39 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
         do_pass<GATED>(a, y - a.extra, 0, u_first, nu, lds);
         return;
     }
-    int *pre = reinterpret_cast<int *>(lds);  // [n + 1], in the scale areas (free until a pass starts)
+    int *pre = reinterpret_cast<int *>(lds + kPreOff);
     const int n = *a.nactive;
-    extra_pass_prefix(a, n, pre);
+    pass_prefix<true>(a, n, pre);
     const int total = pre[n];
     for (int g = y; g < total; g += a.extra) {
-        int lo = 0, hi = n - 1;  // last slot with pre[slot] <= g
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= g) lo = mid;
-            else hi = mid - 1;
-        }
-        const int slot = lo, pass = 1 + g - pre[lo];
-        __syncthreads();  // every thread has read pre[] before a pass reuses the area
-        do_pass<GATED>(a, slot, pass, u_first, nu, lds);
-        if (g + a.extra < total) {
-            __syncthreads();  // the pass's readers of LDS are done
-            extra_pass_prefix(a, n, pre);
-        }
+        const int slot = find_slot(pre, n, g);
+        if (g > y) __syncthreads();  // the previous pass's readers of LDS are done
+        do_pass<GATED>(a, slot, 1 + g - pre[slot], u_first, nu, lds);
+    }
+}
+
+// Persistent mode (large launches).  The work is the list of (pass, unit)
+// items of every active expert, in slot order, each pass staging at most
+// pass_rows routed rows; block b takes the b-th contiguous share of it and
+// streams it pass by pass, so the start-up of a block is paid once per share
+// rather than once per few units.
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
+    extern __shared__ uint4 lds4[];
+    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+    int *pre = reinterpret_cast<int *>(lds + kPreOff);
+    const int n = *a.nactive;
+    pass_prefix<false>(a, n, pre);
+    const int64_t total = (int64_t)pre[n] * a.units;
+    const int64_t i0 = total * blockIdx.x / gridDim.x, i1 = total * (blockIdx.x + 1) / gridDim.x;
+    if (i0 >= i1) return;
+    const int sp0 = (int)(i0 / a.units), sp1 = (int)((i1 - 1) / a.units);
+    for (int sp = sp0; sp <= sp1; ++sp) {
+        const int slot = find_slot(pre, n, sp);
+        const int ua = sp == sp0 ? (int)(i0 - (int64_t)sp0 * a.units) : 0;
+        const int ub = sp == sp1 ? (int)(i1 - (int64_t)sp1 * a.units) : a.units;
+        if (sp > sp0) __syncthreads();  // the previous pass's readers of LDS are done
+        do_pass<GATED>(a, slot, sp - pre[slot], ua, ub - ua, lds);
     }
 }
 
@@ -569,6 +619,15 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.pass_rows = pr;
     const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
     const int cap = E < P ? E : P;
+    const int nblk = 2 * moe_host::cu_count();  // resident blocks: two per CU (LDS, VGPRs)
+    if ((int64_t)cap * a.units > 2 * (int64_t)nblk) {
+        // Persistent: one share of the (pass, unit) list per resident block.
+        if (gated)
+            hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        else
+            hipLaunchKernelGGL(k_decode_row_persist<false>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        return moe_host::launch_status();
+    }
     // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
     // the grid's y extent is kept within its limit by striding over them.
     int extra = (P - 1) / pr;
