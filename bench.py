@@ -16,7 +16,12 @@ instead).  Reported on one JSON line:
   tokens_per_s, pct_of_hbm_peak
   roofline    the dominant kernel (gate+up+SiLU): its algorithmic bytes per
               launch / its mean launch duration, timed with HIP events on the
-              stream it runs on, against 8 TB/s
+              stream it runs on, against 8 TB/s (the many-token K-major
+              workload: its flops per launch against the 2.5 PFLOP/s fp16
+              matrix-core peak); traffic = HBM bytes per launch from the
+              committed counter summary in profiles/ while the kernel sources
+              are unchanged since it was taken, else null
+  hbm_read_ceiling_GBs  a plain 2 GiB streaming read on the same device, as context
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
               same workload, in the same unit
 """
@@ -32,6 +37,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
 METRIC = "expert-weight HBM GB/s (% of peak) + MoE-layer tokens/s, decode batch 1/32"
 
 
@@ -46,7 +52,47 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of one graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile-pass", choices=["gate_up", "copy"], default=None,
+                    help="for counter runs under rocprofv3: launch only gate+up+SiLU (after one sort) "
+                         "--steps times, or a plain 1 GiB device copy --steps times, then exit")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("nvfp4_quantized_moe_amd/csrc/moe_decode_row.hip",
+                  "nvfp4_quantized_moe_amd/csrc/moe_gemm_kmajor.hip",
+                  "nvfp4_quantized_moe_amd/csrc/moe_common.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate+up launch from the committed counter summary of this
+    workload (profiles/traffic_<workload>.txt), or None when there is none or
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def active_weight_bytes(shape, ids) -> int:
@@ -171,6 +217,26 @@ def main():
 
     stream = torch.cuda.Stream()
 
+    if args.profile_pass == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+    if args.profile_pass == "gate_up":
+        with torch.cuda.stream(stream):
+            moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
+                               bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
+            for i in range(args.steps):
+                tabs = layers[i % L][1]
+                moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
+                                           bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
+                                           bufs.active_count, bufs.h, stream)
+        torch.cuda.synchronize()
+        return
+
     def step(i, s):
         bufs.gate, bufs.up, bufs.down = layers[i % L][1]
         b = i % R
@@ -214,23 +280,53 @@ def main():
     value = bytes_timed / (total_ms / 1e3) / 1e9
     tokens_per_s = shape.T * K / (total_ms / 1e3)
 
-    # ---- dominant kernel: gate+up+SiLU launch duration (HIP events on its stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # ---- dominant kernel: gate+up+SiLU launch duration.  HIP events on the
+    # stream it runs on bracket Kr back-to-back launches (one routing batch,
+    # the weight copies cycled as in the timed steps); the mean per launch
+    # includes the short gap between consecutive launches.
+    Kr = min(K, 200)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for i in range(K):
-            bufs.gate, bufs.up, bufs.down = layers[i % L][1]
-            b = i % R
-            moe.moe_nvfp4_sort(ids_d[b], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
-                               bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
-            ev[i][0].record(stream)
-            moe.moe_nvfp4_gate_up_silu(xs[b], shape.k, shape.E, shape.H, shape.I, bufs.gate, bufs.up,
-                                       bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
-                                       bufs.active_count, bufs.h, stream)
-            ev[i][1].record(stream)
+        moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
+                           bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
+        for rep in range(2):  # the first pass warms the launch path
+            e0.record(stream)
+            for i in range(Kr):
+                tabs = layers[i % L][1]
+                moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
+                                           bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
+                                           bufs.active_count, bufs.h, stream)
+            e1.record(stream)
     torch.cuda.synchronize()
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    gu_bytes = float(np.mean([gate_up_bytes(shape, idss[i % R]) for i in range(K)]))
-    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+    gu_ms = e0.elapsed_time(e1) / Kr
+    gu_bytes = float(gate_up_bytes(shape, idss[0]))
+    traffic = measured_traffic(shape.name)
+    if shape.kmajor:
+        # Many-token path: a dense fp16 contraction on the matrix cores.
+        flops = 4.0 * shape.P * shape.I * shape.H  # gate and up, 2 flops per MAC
+        roof = {"bound": "mfma", "achieved": round(flops / (gu_ms / 1e3) / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+        roof["frac"] = round(roof["achieved"] / MFMA_F16_PEAK_TFLOPS, 4)
+        roof["algorithmic_flops_per_launch"] = round(flops)
+    else:
+        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel": "moe_nvfp4_gate_up_silu", "launch_us": round(gu_ms * 1e3, 3),
+                 "algorithmic_bytes_per_launch": round(gu_bytes)})
+
+    # Context: a plain streaming read of 2 GiB (torch's sum) on the same device.
+    big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    big.sum()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        big.sum()
+    r1.record()
+    torch.cuda.synchronize()
+    read_ceiling = 10 * big.numel() * 4 / (r0.elapsed_time(r1) / 1e3) / 1e9
+    del big
 
     line = {
         "metric": METRIC,
@@ -255,17 +351,8 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "active_weight_bytes_per_step": round(bytes_timed / K),
-        "roofline": {
-            "kernel": "moe_nvfp4_gate_up_silu",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "launch_us": round(gu_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": round(gu_bytes),
-        },
+        "roofline": roof,
+        "hbm_read_ceiling_GBs": round(read_ceiling, 1),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

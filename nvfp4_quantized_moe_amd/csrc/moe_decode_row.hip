@@ -53,6 +53,8 @@
 //     of bank conflicts.
 #include "moe_common.hpp"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -136,22 +138,42 @@ __device__ __forceinline__ float absmax8(uint4 v) {
     return fmaxf(a, b);
 }
 
-// Gate+up: rows [row0, row0 + pr) of x -> LDS as bf16 (stride ldx), each
-// row's largest magnitude max-ed into rmax[m] (float bits).  Lane m < 16 of
-// each wave holds the token of row m in tokv.
-// Down: only the maxima of rows [row0, row0 + pr) of h.
-template <bool GATED>
-__device__ __forceinline__ void stage_rows(const DecArgs &a, int row0, int pr, int tokv, uint16_t *xs,
-                                           uint32_t *rmax) {
+__device__ __forceinline__ float absmax8f(const f32x4_t &a, const f32x4_t &b) {
+    const float u = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
+    const float v = fmaxf(fmaxf(fabsf(b[0]), fabsf(b[1])), fmaxf(fabsf(b[2]), fabsf(b[3])));
+    return fmaxf(u, v);
+}
+
+// 8 fp32 values times f -> fp16, written as one 16-byte LDS chunk.
+__device__ __forceinline__ void put_f16x8(uint16_t *dst, const f32x4_t &a, const f32x4_t &b, float f) {
+    f16x8_t h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (_Float16)(a[j] * f);
+        h[4 + j] = (_Float16)(b[j] * f);
+    }
+    *reinterpret_cast<f16x8_t *>(dst) = h;
+}
+
+// Stage rows [row0, row0 + pr) of the activation into LDS as fp16 (stride
+// ldx), row m scaled by 2^-e(m) where e(m) comes from the row's largest
+// magnitude (kept in rmax[m] as float bits; rmax is zero on entry).  Gate+up
+// gathers x rows by token (lane m < 16 of each wave holds row m's token in
+// tokv); down reads h rows in order.  mid() is called once the first loads
+// are in flight and before any is consumed, so the caller can queue more
+// loads behind them.  Ends with the rows visible to the whole block.
+template <bool GATED, typename Mid>
+__device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int tokv, uint16_t *xs, uint32_t *rmax,
+                                      Mid &&mid) {
     const int K = a.K, ldx = a.ldx;
     const int cpr = K >> 3;  // 8-element chunks per row
     const int nch = pr * cpr;
     constexpr int SB = GATED ? 8 : 4;  // chunks per thread per batch
-    for (int base = 0; base < nch; base += kThreads * SB) {
-        int row[SB];
-        float mx[SB];
-        if constexpr (GATED) {
-            int dst[SB];
+    // Unconditional LDS writes throughout: a chunk past the end re-writes
+    // chunk 0 with its own value, and no load is left in flight on any path.
+    if constexpr (GATED) {
+        auto batch = [&](int base, auto first) {
+            int dst[SB], row[SB];
             u32x4_t raw[SB];
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
@@ -163,50 +185,22 @@ __device__ __forceinline__ void stage_rows(const DecArgs &a, int row0, int pr, i
                 const int tok = __builtin_amdgcn_ds_bpermute(4 * m, tokv);
                 raw[i] = moe::gload<u32x4_t>(static_cast<const uint16_t *>(a.act) + (size_t)tok * K + 8 * kc);
             }
-            // Unconditional: a chunk past the end re-writes chunk 0 with its
-            // own value, and no load of the batch is left in flight on any path.
+            if constexpr (decltype(first)::value) mid();
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
                 const uint4 v = uint4{raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
                 *reinterpret_cast<uint4 *>(xs + dst[i]) = v;
-                mx[i] = absmax8(v);
+                atomicMax(rmax + row[i], __float_as_uint(absmax8(v)));
             }
-        } else {
-            f32x4_t f0[SB], f1[SB];
-#pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int idx = base + i * kThreads + (int)threadIdx.x;
-                const int ic = idx < nch ? idx : 0;
-                const int m = ic / cpr, kc = ic - m * cpr;
-                row[i] = m;
-                const float *src = static_cast<const float *>(a.act) + (size_t)(row0 + m) * K + 8 * kc;
-                f0[i] = moe::gload<f32x4_t>(src);
-                f1[i] = moe::gload<f32x4_t>(src + 4);
-            }
-#pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const float a0 = fmaxf(fmaxf(fabsf(f0[i][0]), fabsf(f0[i][1])), fmaxf(fabsf(f0[i][2]), fabsf(f0[i][3])));
-                const float a1 = fmaxf(fmaxf(fabsf(f1[i][0]), fabsf(f1[i][1])), fmaxf(fabsf(f1[i][2]), fabsf(f1[i][3])));
-                mx[i] = fmaxf(a0, a1);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(mx[i]));
-    }
-}
-
-// Gate+up: the staged bf16 rows -> fp16 in place, row m scaled by 2^-e(m).
-// Down: rows of h read again and written to LDS as fp16, scaled the same way.
-template <bool GATED>
-__device__ __forceinline__ void rows_to_f16(const DecArgs &a, int row0, int pr, uint16_t *xs,
-                                            const uint32_t *rmax) {
-    const int K = a.K, cpr = K >> 3;
-    const int nch = pr * cpr;
-    if constexpr (GATED) {
-        for (int idx = threadIdx.x; idx < nch; idx += kThreads) {
+        };
+        // The first batch is peeled so that mid() sits on a single path.
+        batch(0, std::true_type{});
+        for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
+        __syncthreads();  // bf16 rows and their maxima are complete
+        for (int idx = threadIdx.x; idx < nch; idx += kThreads) {  // bf16 -> scaled fp16 in place
             const int m = idx / cpr, kc = idx - m * cpr;
             const float f = exp2i(-row_exp(rmax[m]));
-            uint4 *p = reinterpret_cast<uint4 *>(xs + m * a.ldx + 8 * kc);
+            uint4 *p = reinterpret_cast<uint4 *>(xs + m * ldx + 8 * kc);
             const uint4 v = *p;
             const uint32_t u[4] = {v.x, v.y, v.z, v.w};
             f16x8_t h;
@@ -217,34 +211,78 @@ __device__ __forceinline__ void rows_to_f16(const DecArgs &a, int row0, int pr, 
             }
             *reinterpret_cast<f16x8_t *>(p) = h;
         }
+        __syncthreads();
     } else {
-        constexpr int SB = 4;
-        for (int base = 0; base < nch; base += kThreads * SB) {
-            int dst[SB];
-            float f[SB];
+        const float *h = static_cast<const float *>(a.act);
+        auto chunk = [&](int idx, int &m, int &kc) {
+            const int ic = idx < nch ? idx : 0;
+            m = ic / cpr;
+            kc = ic - m * cpr;
+        };
+        if (nch <= kThreads * SB) {
+            // One batch: the rows stay in registers between the two phases.
+            int row[SB];
             f32x4_t f0[SB], f1[SB];
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
-                const int idx = base + i * kThreads + (int)threadIdx.x;
-                const int ic = idx < nch ? idx : 0;
-                const int m = ic / cpr, kc = ic - m * cpr;
-                dst[i] = m * a.ldx + 8 * kc;
-                f[i] = exp2i(-row_exp(rmax[m]));
-                const float *src = static_cast<const float *>(a.act) + (size_t)(row0 + m) * K + 8 * kc;
+                int m, kc;
+                chunk(i * kThreads + (int)threadIdx.x, m, kc);
+                row[i] = m;
+                const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
                 f0[i] = moe::gload<f32x4_t>(src);
                 f1[i] = moe::gload<f32x4_t>(src + 4);
             }
+            mid();
+#pragma unroll
+            for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+            __syncthreads();  // maxima complete
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
-                f16x8_t h;
+                const int idx = i * kThreads + (int)threadIdx.x;
+                const int ic = idx < nch ? idx : 0;
+                const int kc = ic - row[i] * cpr;
+                put_f16x8(xs + row[i] * ldx + 8 * kc, f0[i], f1[i], exp2i(-row_exp(rmax[row[i]])));
+            }
+        } else {
+            // Several batches: maxima first, then the rows read again (L2 hits).
+            auto batch = [&](int base, auto first) {
+                int row[SB];
+                f32x4_t f0[SB], f1[SB];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j] = (_Float16)(f0[i][j] * f[i]);
-                    h[4 + j] = (_Float16)(f1[i][j] * f[i]);
+                for (int i = 0; i < SB; ++i) {
+                    int m, kc;
+                    chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
+                    row[i] = m;
+                    const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
+                    f0[i] = moe::gload<f32x4_t>(src);
+                    f1[i] = moe::gload<f32x4_t>(src + 4);
                 }
-                *reinterpret_cast<f16x8_t *>(xs + dst[i]) = h;  // unconditional, as above
+                if constexpr (decltype(first)::value) mid();
+#pragma unroll
+                for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+            };
+            batch(0, std::true_type{});
+            for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
+            __syncthreads();  // maxima complete
+            for (int base = 0; base < nch; base += kThreads * SB) {
+                int dst[SB];
+                float fs[SB];
+                f32x4_t f0[SB], f1[SB];
+#pragma unroll
+                for (int i = 0; i < SB; ++i) {
+                    int m, kc;
+                    chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
+                    dst[i] = m * ldx + 8 * kc;
+                    fs[i] = exp2i(-row_exp(rmax[m]));
+                    const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
+                    f0[i] = moe::gload<f32x4_t>(src);
+                    f1[i] = moe::gload<f32x4_t>(src + 4);
+                }
+#pragma unroll
+                for (int i = 0; i < SB; ++i) put_f16x8(xs + dst[i], f0[i], f1[i], fs[i]);
             }
         }
+        __syncthreads();
     }
 }
 
@@ -323,16 +361,20 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     int tokv = 0;  // gate+up: token of row (lane & 15) of the pass
     if constexpr (GATED) tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
     __syncthreads();  // rmax cleared
+    // The first ring slot, then the activation loads, then the rest of the
+    // ring: the activations wait only for slot 0, and while they are
+    // converted the rest of the ring is in flight.
     __builtin_amdgcn_sched_barrier(0);
+    load(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        load(d);
-        __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-    }
-    stage_rows<GATED>(a, row0, pr, tokv, xs, rmax);
-    __syncthreads();  // staged rows and their maxima are complete
-    rows_to_f16<GATED>(a, row0, pr, xs, rmax);
-    __syncthreads();  // fp16 rows are visible
+        for (int d = 1; d < D; ++d) {
+            load(d);
+            __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+        }
+    });
 
     const int TG = (pr + 3) >> 2;
     const int tA = n >> 2, cA = n & 3;  // A-operand role: token tA of each group, quarter cA
@@ -352,106 +394,110 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     for (int tg = 0; tg < kMaxTG; ++tg) acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     int cu = 0, ci = 0;  // stream position being computed
-    // The trip count is padded to a multiple of the ring and every step refills
-    // its slot, so the loop body has no branch around a load.
-    for (int base = 0; base < total; base += D) {
+    // One step of the ring: compute slot d, then (refill) load the step D
+    // ahead into it.  Every iteration but the last refills all of its slots,
+    // so the loop body has no branch around a load; the last iteration, whose
+    // refills would all lie past the end, has none.
+    auto step = [&](const int d, auto refill) {
+        if (d % kGroup == 0) {
+            // This group's scale slices -> LDS (undoing a clamped load's shift).
+            const u32x4_t v = sv[d / kGroup];
+            const int s = ssh[d / kGroup];
+            u32x4_t r;
+            r[0] = s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3]));
+            r[1] = s == 0 ? v[1] : (s == 1 ? v[2] : v[3]);
+            r[2] = s == 0 ? v[2] : v[3];
+            r[3] = v[3];
+            *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
+        }
+        // A fragments of token group 0 (always present), read first so the
+        // LDS latency hides behind the decode.
+        const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
+        const int kac = ka < K ? ka : 0;              // past the end: any finite row data
+        f16x8_t a0[4];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            if (d % kGroup == 0) {
-                // This group's scale slices -> LDS (undoing a clamped load's shift).
-                const u32x4_t v = sv[d / kGroup];
-                const int s = ssh[d / kGroup];
-                u32x4_t r;
-                r[0] = s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3]));
-                r[1] = s == 0 ? v[1] : (s == 1 ? v[2] : v[3]);
-                r[2] = s == 0 ? v[2] : v[3];
-                r[3] = v[3];
-                *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
+        for (int ks = 0; ks < 4; ++ks) a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + arow[0] + kac + 8 * ks);
+        const int kq = 512 * ci + 128 * q + 32 * c;  // first k of this lane's B chunk
+        const bool kin = cu < nu && kq < K;
+        const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
+        const uint32_t v0 = *reinterpret_cast<const uint16_t *>(sp);
+        const uint32_t v1 = *reinterpret_cast<const uint16_t *>(sp + 128);
+        const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
+        const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, 1.0f, false) : zero2;
+        const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, 1.0f, false) : zero2;
+        const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
+        const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
+        f16x8_t b0[4], b1[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            b0[ks] = decode_b(w0[d][ks], ks < 2 ? sl0 : sh0);
+            b1[ks] = decode_b(w1[d][ks], ks < 2 ? sl1 : sh1);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            acc0[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0[0], 0, 0, 0);
+            acc1[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1[0], 0, 0, 0);
+        }
+#pragma unroll
+        for (int tg = 1; tg < kMaxTG; ++tg) {
+            if (tg < TG) {
+                const uint16_t *ap = xs + arow[tg] + kac;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const f16x8_t A = *reinterpret_cast<const f16x8_t *>(ap + 8 * ks);
+                    acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b0[ks], acc0[tg], 0, 0, 0);
+                    acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b1[ks], acc1[tg], 0, 0, 0);
+                }
             }
-            // A fragments of token group 0 (always present), read first so the
-            // LDS latency hides behind the decode.
-            const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
-            const int kac = ka < K ? ka : 0;              // past the end: any finite row data
-            f16x8_t a0[4];
+        }
+        if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
+            const int unit = u_first + cu;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + arow[0] + kac + 8 * ks);
-            const int kq = 512 * ci + 128 * q + 32 * c;  // first k of this lane's B chunk
-            const bool kin = cu < nu && kq < K;
-            const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
-            const uint32_t v0 = *reinterpret_cast<const uint16_t *>(sp);
-            const uint32_t v1 = *reinterpret_cast<const uint16_t *>(sp + 128);
-            const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
-            const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, 1.0f, false) : zero2;
-            const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, 1.0f, false) : zero2;
-            const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
-            const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
-            f16x8_t b0[4], b1[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                b0[ks] = decode_b(w0[d][ks], ks < 2 ? sl0 : sh0);
-                b1[ks] = decode_b(w1[d][ks], ks < 2 ? sl1 : sh1);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                acc0[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0[0], 0, 0, 0);
-                acc1[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1[0], 0, 0, 0);
-            }
-#pragma unroll
-            for (int tg = 1; tg < kMaxTG; ++tg) {
+            for (int tg = 0; tg < kMaxTG; ++tg) {
                 if (tg < TG) {
-                    const uint16_t *ap = xs + arow[tg] + kac;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const f16x8_t A = *reinterpret_cast<const f16x8_t *>(ap + 8 * ks);
-                        acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b0[ks], acc0[tg], 0, 0, 0);
-                        acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b1[ks], acc1[tg], 0, 0, 0);
-                    }
-                }
-            }
-            if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
-                const int unit = u_first + cu;
-#pragma unroll
-                for (int tg = 0; tg < kMaxTG; ++tg) {
-                    if (tg < TG) {
-                        // Lane (n, t) holds rows 4t..4t+3 of column n; the kept
-                        // block is row 4t + (n & 3).  Sum the quarters of a quad.
-                        const float g0 = moe::group_sum<4>(pick(acc0[tg], c)) * oscale[tg];
-                        const float g1 = moe::group_sum<4>(pick(acc1[tg], c)) * oscale[tg];
-                        const int tl = 4 * tg + q;
-                        if (c == 0 && tl < pr) {
-                            float *o = a.out + (size_t)(row0 + tl) * N;
-                            if constexpr (GATED) {
-                                o[16 * unit + 4 * w + rho] = moe::silu_f32(g0 * s2A) * (g1 * s2B);
-                            } else {
-                                o[32 * unit + 8 * w + rho] = g0 * s2A;
-                                o[32 * unit + 8 * w + 4 + rho] = g1 * s2A;
-                            }
+                    // Lane (n, t) holds rows 4t..4t+3 of column n; the kept
+                    // block is row 4t + (n & 3).  Sum the quarters of a quad.
+                    const float g0 = moe::group_sum<4>(pick(acc0[tg], c)) * oscale[tg];
+                    const float g1 = moe::group_sum<4>(pick(acc1[tg], c)) * oscale[tg];
+                    const int tl = 4 * tg + q;
+                    if (c == 0 && tl < pr) {
+                        float *o = a.out + (size_t)(row0 + tl) * N;
+                        if constexpr (GATED) {
+                            o[16 * unit + 4 * w + rho] = moe::silu_f32(g0 * s2A) * (g1 * s2B);
+                        } else {
+                            o[32 * unit + 8 * w + rho] = g0 * s2A;
+                            o[32 * unit + 8 * w + 4 + rho] = g1 * s2A;
                         }
-                        acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                     }
+                    acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
             }
-            if (++ci == nseg) {
-                ci = 0;
-                ++cu;
-            }
+        }
+        if (++ci == nseg) {
+            ci = 0;
+            ++cu;
+        }
+        if constexpr (decltype(refill)::value) {
             // Loads keep their order; arithmetic and LDS work may move across.
             __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
             load(d);
             __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
         }
+    };
+    int base = 0;
+    for (; base + D < total; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) step(d, std::true_type{});
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(d, std::false_type{});
 }
 
-// Passes of an expert with r routed rows: all of them, or those beyond the first.
-template <bool FURTHER>
-__device__ __forceinline__ int passes_of(int r, int pr) {
-    return r <= 0 ? 0 : (FURTHER ? (r - 1) / pr : (r + pr - 1) / pr);
-}
+// Passes beyond the first of an expert with r routed rows.
+__device__ __forceinline__ int further_passes(int r, int pr) { return r <= 0 ? 0 : (r - 1) / pr; }
 
-// Block-wide exclusive prefix sum over the active slots of passes_of<FURTHER>:
+// Block-wide exclusive prefix sum over the active slots of further_passes:
 // pre[s] for s < n, pre[n] = total.  n <= 1024.
-template <bool FURTHER>
 __device__ __forceinline__ void pass_prefix(const DecArgs &a, int n, int *pre) {
     __shared__ int wsum[kWaves];
     const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
@@ -464,7 +510,7 @@ __device__ __forceinline__ void pass_prefix(const DecArgs &a, int n, int *pre) {
             const int e = a.active[sl];
             r = a.offsets[e + 1] - a.offsets[e];
         }
-        c[i] = passes_of<FURTHER>(r, a.pass_rows);
+        c[i] = further_passes(r, a.pass_rows);
         sum += c[i];
     }
     int incl = sum;  // inclusive scan over the wave
@@ -525,7 +571,7 @@ __device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, in
     run_pass<GATED, kDepth>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
 }
 
-// Grid mode (small launches).  Block (x, y): units [x G, x G + G) of
+// Block (x, y): units [x G, x G + G) of
 //   y >= extra: the first pass (rows 0 .. pass_rows) of active slot y - extra;
 //   y <  extra: further passes number y, y + extra, ... in slot order, so an
 //               expert with many routed rows is spread over many blocks of
@@ -544,37 +590,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     }
     int *pre = reinterpret_cast<int *>(lds + kPreOff);
     const int n = *a.nactive;
-    pass_prefix<true>(a, n, pre);
+    pass_prefix(a, n, pre);
     const int total = pre[n];
     for (int g = y; g < total; g += a.extra) {
         const int slot = find_slot(pre, n, g);
         if (g > y) __syncthreads();  // the previous pass's readers of LDS are done
         do_pass<GATED>(a, slot, 1 + g - pre[slot], u_first, nu, lds);
-    }
-}
-
-// Persistent mode (large launches).  The work is the list of (pass, unit)
-// items of every active expert, in slot order, each pass staging at most
-// pass_rows routed rows; block b takes the b-th contiguous share of it and
-// streams it pass by pass, so the start-up of a block is paid once per share
-// rather than once per few units.
-template <bool GATED>
-__global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
-    extern __shared__ uint4 lds4[];
-    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
-    int *pre = reinterpret_cast<int *>(lds + kPreOff);
-    const int n = *a.nactive;
-    pass_prefix<false>(a, n, pre);
-    const int64_t total = (int64_t)pre[n] * a.units;
-    const int64_t i0 = total * blockIdx.x / gridDim.x, i1 = total * (blockIdx.x + 1) / gridDim.x;
-    if (i0 >= i1) return;
-    const int sp0 = (int)(i0 / a.units), sp1 = (int)((i1 - 1) / a.units);
-    for (int sp = sp0; sp <= sp1; ++sp) {
-        const int slot = find_slot(pre, n, sp);
-        const int ua = sp == sp0 ? (int)(i0 - (int64_t)sp0 * a.units) : 0;
-        const int ub = sp == sp1 ? (int)(i1 - (int64_t)sp1 * a.units) : a.units;
-        if (sp > sp0) __syncthreads();  // the previous pass's readers of LDS are done
-        do_pass<GATED>(a, slot, sp - pre[slot], ua, ub - ua, lds);
     }
 }
 
@@ -603,9 +624,14 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.K = K;
     const int ucols = gated ? 16 : 32;
     a.units = (N + ucols - 1) / ucols;
-    // Units per block: about 32 blocks along N per expert, at most 4 units each.
-    int G = a.units / 32;
-    G = G < 1 ? 1 : (G > 4 ? 4 : G);
+    const int cap = E < P ? E : P;
+    // Units per block: about 32 ring steps per wave, so a block's start-up
+    // (tables, activation staging, first loads) is paid over enough streaming;
+    // fewer when the grid would otherwise not fill two blocks per CU.
+    const int nseg = (K / 2 + 255) / 256;
+    int G = (32 + nseg - 1) / nseg;
+    G = G < 1 ? 1 : (G > 8 ? 8 : G);
+    while (G > 1 && (int64_t)cap * ((a.units + G - 1) / G) < 2 * (int64_t)moe_host::cu_count()) --G;
     a.G = G;
     // Staged row stride: 2K bytes padded to 16 mod 256, so the 16 lanes of an
     // A-operand read (4 rows x 4 quarters, 64 bytes apart) hit distinct banks.
@@ -618,16 +644,6 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     if (pr > P) pr = P;
     a.pass_rows = pr;
     const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
-    const int cap = E < P ? E : P;
-    const int nblk = 2 * moe_host::cu_count();  // resident blocks: two per CU (LDS, VGPRs)
-    if ((int64_t)cap * a.units > 2 * (int64_t)nblk) {
-        // Persistent: one share of the (pass, unit) list per resident block.
-        if (gated)
-            hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
-        else
-            hipLaunchKernelGGL(k_decode_row_persist<false>, dim3(nblk), dim3(kThreads), lds, stream, a);
-        return moe_host::launch_status();
-    }
     // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
     // the grid's y extent is kept within its limit by striding over them.
     int extra = (P - 1) / pr;
