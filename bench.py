@@ -64,13 +64,19 @@ KERNEL_SOURCES = ("nvfp4_quantized_moe_amd/csrc/moe_decode_row.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    an edit to a comment does not invalidate the counters."""
     import hashlib
+    import re
 
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

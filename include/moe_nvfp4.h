@@ -10,7 +10,7 @@
  *   moe_nvfp4_blend         out[t] = sum_j w[t, j] * y[pair of (t, j)]
  *
  * plus a load-time byte transpose, transpose_u8, that builds the K-major
- * "transposed twin" of a weight for the many-token path.
+ * transposed twin of a weight for the many-token path.
  *
  * Sources of the operations (the reference pages are Rust source pages of a
  * model runtime; each is cited by its file name and the item on it):

@@ -1,5 +1,5 @@
 // Many-token path: grouped NVFP4 GEMM on the matrix cores, reading the
-// K-major "transposed twin" of each expert weight (packed [K/2, N], scales
+// K-major transposed twin of each expert weight (packed [K/2, N], scales
 // [K/16, N]; transpose.rs, transpose_for_gemm, and prefill_weights.rs,
 // prepare_prefill_weights, which builds these twins for the sorted prefill
 // path).  Same operation as the decode GEMV: gate+up with the fused SiLU

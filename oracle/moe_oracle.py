@@ -10,9 +10,9 @@ What it computes is the plain definition of a top-k routed SwiGLU
 mixture-of-experts over NVFP4-dequantised weights, in float64, step by step:
 
   1. NVFP4 decode (quant_shard.rs page, the layout comment above
-     ``shard_quantized_nvfp4``; nvfp4_moe_grouped.rs page, module doc:
-     "packed E2M1, E4M3 block scales of 16, per-tensor scale 2"; expert.rs
-     page, ``QuantWeight::Nvfp4`` doc): W[n, k] = e2m1(nibble) *
+     ``shard_quantized_nvfp4``; nvfp4_moe_grouped.rs page, module doc, which
+     names the three parts: E2M1 codes, one E4M3 scale per 16 values and one
+     f32 scale per tensor; expert.rs page, ``QuantWeight::Nvfp4`` doc): W[n, k] = e2m1(nibble) *
      e4m3(scale[n, k // 16]) * scale_2.  The transposed twin
      (transpose.rs page, ``transpose_for_gemm``) stores the same bytes at
      [k // 2, n] and [k // 16, n].
@@ -29,8 +29,8 @@ Readings where the pages are silent (each listed in the design notes):
   * E2M1 is the OCP FP4 format (1 sign, 2 exponent bits with bias 1,
     1 mantissa bit; code 0b?001 is the subnormal 0.5).
   * E4M3 is the OCP "FN" variant: bias 7, subnormals, no infinities, NaN
-    only at S.1111.111, largest finite 448 (the pages' "saturating at 448",
-    prefill_weights.rs page, doc of the shared-expert copies).
+    only at S.1111.111, largest finite 448 (prefill_weights.rs page, the
+    shared-expert copies, gives 448 as the E4M3 saturation point).
   * The low nibble of a packed byte holds the even k.
   * The sort is stable by flat pair index t*k + j; active experts ascend.
   * Pairs whose expert id lies outside [0, E) belong to no expert: they

@@ -281,3 +281,13 @@ def test_row_major_activation_range():
         parity.assert_parity_relative(y[p], ref["y"][p], f"y row {p}")
     for t in range(shape.T):
         parity.assert_parity_relative(out[t], ref["out"][t], f"out row {t}")
+
+
+@pytest.mark.parametrize("routing", ["uniform", "zipf"])
+def test_row_major_many_experts_and_passes(routing):
+    """64 experts, 800 routed rows: several units per block, and with
+    Zipf-skewed routing experts whose rows take several passes on extra
+    block rows."""
+    say("many experts and passes", routing)
+    shape = synth.MoeShape(f"wide_{routing}", 200, 768, 1024, 64, 4, routing, False)
+    _full_check(Case(17, shape), f"wide {routing}")
