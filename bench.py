@@ -21,7 +21,6 @@ instead).  Reported on one JSON line:
               matrix-core peak); traffic = HBM bytes per launch from the
               committed counter summary in profiles/ while the kernel sources
               are unchanged since it was taken, else null
-  hbm_read_ceiling_GBs  a plain 2 GiB streaming read on the same device, as context
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
               same workload, in the same unit
 """
@@ -321,18 +320,6 @@ def main():
     roof.update({"traffic": traffic, "kernel": "moe_nvfp4_gate_up_silu", "launch_us": round(gu_ms * 1e3, 3),
                  "algorithmic_bytes_per_launch": round(gu_bytes)})
 
-    # Context: a plain streaming read of 2 GiB (torch's sum) on the same device.
-    big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
-    big.sum()
-    torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for _ in range(10):
-        big.sum()
-    r1.record()
-    torch.cuda.synchronize()
-    read_ceiling = 10 * big.numel() * 4 / (r0.elapsed_time(r1) / 1e3) / 1e9
-    del big
 
     line = {
         "metric": METRIC,
@@ -358,7 +345,6 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "active_weight_bytes_per_step": round(bytes_timed / K),
         "roofline": roof,
-        "hbm_read_ceiling_GBs": round(read_ceiling, 1),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
