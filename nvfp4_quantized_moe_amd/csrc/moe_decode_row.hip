@@ -155,6 +155,27 @@ __device__ __forceinline__ void put_f16x8(uint16_t *dst, const f32x4_t &a, const
     *reinterpret_cast<f16x8_t *>(dst) = h;
 }
 
+// Max-merge v (a non-negative float's bits) into rmax[m] for the 64 lanes of
+// a wave holding consecutive chunks, so m takes at most a few consecutive
+// values: the first and the last lane's rows get one atomic each after a wave
+// reduction; lanes of any row strictly between (short rows only) post their
+// own.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+__device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v) {
+    const int lane = threadIdx.x & 63;
+    const int m_lo = __builtin_amdgcn_readfirstlane(m);
+    const int m_hi = __builtin_amdgcn_readlane(m, 63);
+    const uint32_t lo = wave_max_u32(m == m_lo ? v : 0u);
+    const uint32_t hi = wave_max_u32(m == m_hi ? v : 0u);
+    if (lane == 0) atomicMax(rmax + m_lo, lo);
+    if (lane == 63 && m_hi != m_lo) atomicMax(rmax + m_hi, hi);
+    if (m != m_lo && m != m_hi) atomicMax(rmax + m, v);
+}
+
 // Stage rows [row0, row0 + pr) of the activation into LDS as fp16 (stride
 // ldx), row m scaled by 2^-e(m) where e(m) comes from the row's largest
 // magnitude (kept in rmax[m] as float bits; rmax is zero on entry).  Gate+up
@@ -173,24 +194,23 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
     // chunk 0 with its own value, and no load is left in flight on any path.
     if constexpr (GATED) {
         auto batch = [&](int base, auto first) {
-            int dst[SB], row[SB];
+            int ic[SB];
             u32x4_t raw[SB];
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
                 const int idx = base + i * kThreads + (int)threadIdx.x;
-                const int ic = idx < nch ? idx : 0;
-                const int m = ic / cpr, kc = ic - m * cpr;
-                row[i] = m;
-                dst[i] = m * ldx + 8 * kc;
+                ic[i] = idx < nch ? idx : 0;
+                const int m = ic[i] / cpr, kc = ic[i] - m * cpr;
                 const int tok = __builtin_amdgcn_ds_bpermute(4 * m, tokv);
                 raw[i] = moe::gload<u32x4_t>(static_cast<const uint16_t *>(a.act) + (size_t)tok * K + 8 * kc);
             }
             if constexpr (decltype(first)::value) mid();
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
+                const int m = ic[i] / cpr, kc = ic[i] - m * cpr;
                 const uint4 v = uint4{raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
-                *reinterpret_cast<uint4 *>(xs + dst[i]) = v;
-                atomicMax(rmax + row[i], __float_as_uint(absmax8(v)));
+                *reinterpret_cast<uint4 *>(xs + m * ldx + 8 * kc) = v;
+                row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
             }
         };
         // The first batch is peeled so that mid() sits on a single path.
@@ -234,7 +254,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
             }
             mid();
 #pragma unroll
-            for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+            for (int i = 0; i < SB; ++i) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
             __syncthreads();  // maxima complete
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
@@ -259,7 +279,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                 }
                 if constexpr (decltype(first)::value) mid();
 #pragma unroll
-                for (int i = 0; i < SB; ++i) atomicMax(rmax + row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+                for (int i = 0; i < SB; ++i) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
             };
             batch(0, std::true_type{});
             for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
@@ -599,6 +619,130 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     }
 }
 
+// Relative cost of one unit of a pass with r routed rows (token groups of 4
+// share each decoded weight; the weight stream itself costs the same).
+__device__ __forceinline__ int unit_cost(int r) { return 3 + ((r + 3) >> 2); }
+
+// Rows of active slot s.
+__device__ __forceinline__ int slot_rows(const DecArgs &a, int s) {
+    const int e = a.active[s];
+    return a.offsets[e + 1] - a.offsets[e];
+}
+
+// Block-wide exclusive prefix sum over the active slots of the cost of all
+// their passes (units x unit_cost per pass): pre[s] for s < n, pre[n] = total.
+__device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre) {
+    __shared__ int wsum[kWaves];
+    const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
+    const int pr = a.pass_rows;
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * t + i;
+        int cost = 0;
+        if (sl < n) {
+            const int r = slot_rows(a, sl);
+            const int full = r / pr, rem = r - full * pr;
+            cost = a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0));
+        }
+        c[i] = cost;
+        sum += cost;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += wsum[i];
+    int run = base + incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * t + i;
+        if (sl < n) pre[sl] = run;
+        run += c[i];
+    }
+    if (t == kThreads - 1) pre[n] = run;
+    __syncthreads();
+}
+
+// The first unit, in (slot, pass, unit) order, whose cost-weighted start is
+// at or after c; s == n when there is none.
+struct Cursor {
+    int s, p, u;
+};
+__device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, int n, int c) {
+    Cursor k{n, 0, 0};
+    if (c >= pre[n]) return k;
+    int s = find_slot(pre, n, c);
+    int rem = c - pre[s];
+    const int pr = a.pass_rows;
+    int r = slot_rows(a, s);
+    int p = 0;
+    for (;;) {
+        if (p * pr >= r) {  // past the slot's last pass: first unit of the next slot
+            ++s;
+            p = 0;
+            if (s >= n) break;
+            r = slot_rows(a, s);
+            rem = 0;
+            continue;
+        }
+        const int w = unit_cost(min(pr, r - p * pr));
+        if (rem >= a.units * w) {
+            rem -= a.units * w;
+            ++p;
+            continue;
+        }
+        const int u = (rem + w - 1) / w;
+        if (u >= a.units) {
+            ++p;
+            rem = 0;
+            continue;
+        }
+        k = Cursor{s, p, u};
+        return k;
+    }
+    return Cursor{n, 0, 0};
+}
+
+// Persistent mode (launches with plenty of work).  The work is the list of
+// (slot, pass, unit) in order, each unit weighted by unit_cost of its pass;
+// block b takes the units whose weighted start lies in the b-th equal share,
+// and streams them pass by pass.  Every block is busy for about the same
+// time and no block is launched only to find no work.
+template <bool GATED>
+__global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
+    extern __shared__ uint4 lds4[];
+    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+    int *pre = reinterpret_cast<int *>(lds + kPreOff);
+    const int n = *a.nactive;
+    cost_prefix(a, n, pre);
+    const int total = pre[n];
+    const int c0 = (int)((int64_t)total * blockIdx.x / gridDim.x);
+    const int c1 = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+    Cursor k = locate(a, pre, n, c0);
+    const Cursor end = locate(a, pre, n, c1);
+    bool first = true;
+    while (k.s < n && (k.s < end.s || (k.s == end.s && (k.p < end.p || (k.p == end.p && k.u < end.u))))) {
+        const bool last_item = k.s == end.s && k.p == end.p;
+        const int ub = last_item ? end.u : a.units;
+        if (!first) __syncthreads();  // the previous pass's readers of LDS are done
+        first = false;
+        do_pass<GATED>(a, k.s, k.p, k.u, ub - k.u, lds);
+        // next (slot, pass)
+        const int r = slot_rows(a, k.s);
+        if ((k.p + 1) * a.pass_rows < r) {
+            k = Cursor{k.s, k.p + 1, 0};
+        } else {
+            k = Cursor{k.s + 1, 0, 0};
+        }
+    }
+}
+
 }  // namespace
 
 // Launch the row-major grouped projection (used by the two C-ABI entry points).
@@ -644,6 +788,18 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     if (pr > P) pr = P;
     a.pass_rows = pr;
     const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
+    // Persistent mode when the grid would hold many blocks per resident slot
+    // and the weighted work count fits an int.
+    const int nblk = 2 * moe_host::cu_count();
+    const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
+    if ((int64_t)cap * ((a.units + G - 1) / G) > 2 * (int64_t)nblk &&
+        max_passes * a.units * 7 < ((int64_t)1 << 31)) {
+        if (gated)
+            hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        else
+            hipLaunchKernelGGL(k_decode_row_persist<false>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        return moe_host::launch_status();
+    }
     // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
     // the grid's y extent is kept within its limit by striding over them.
     int extra = (P - 1) / pr;
