@@ -8,7 +8,7 @@
 
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
-                          const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
+                          const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
                           hipStream_t stream);
 int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                            const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
@@ -43,7 +43,7 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
     const int P = T * k;
     if (gate.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
-                                     gate, &up, h, I, H, P, E, (hipStream_t)stream);
+                                     gate, &up, h, I, H, T, P, E, (hipStream_t)stream);
     return moe_launch_gemm_kmajor(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
                                   &up, h, I, H, P, E, (hipStream_t)stream);
 }
@@ -59,7 +59,7 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
     const int P = T * k;
     if (down.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
-                                     nullptr, y, H, I, P, E, (hipStream_t)stream);
+                                     nullptr, y, H, I, T, P, E, (hipStream_t)stream);
     return moe_launch_gemm_kmajor(false, h, nullptr, expert_offsets, active_experts, active_count, down,
                                   nullptr, y, H, I, P, E, (hipStream_t)stream);
 }

@@ -22,15 +22,29 @@ __global__ __launch_bounds__(kBlendThreads) void k_moe_blend(const float *__rest
     uint16_t *o = out + (size_t)t * H;
     if ((H & 3) == 0) {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int p = pp[j];
-            if (p < 0) continue;
-            const float wj = wt[j];
-            const float4 v = *reinterpret_cast<const float4 *>(y + (size_t)p * H + n);
-            a0 = fmaf(wj, v.x, a0);
-            a1 = fmaf(wj, v.y, a1);
-            a2 = fmaf(wj, v.z, a2);
-            a3 = fmaf(wj, v.w, a3);
+        // Eight pairs at a time: their positions and weights first, then all
+        // eight rows of y, so the loads of a token overlap instead of chaining.
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int p[8];
+            float wj[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool in = j0 + i < k;
+                p[i] = in ? pp[j0 + i] : -1;
+                wj[i] = in ? wt[j0 + i] : 0.f;
+            }
+            float4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)  // a pair of no expert reads row 0 and adds nothing
+                v[i] = *reinterpret_cast<const float4 *>(y + (size_t)(p[i] < 0 ? 0 : p[i]) * H + n);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (p[i] < 0) continue;
+                a0 = fmaf(wj[i], v[i].x, a0);
+                a1 = fmaf(wj[i], v[i].y, a1);
+                a2 = fmaf(wj[i], v[i].z, a2);
+                a3 = fmaf(wj[i], v[i].w, a3);
+            }
         }
         uint2 r;
         r.x = (uint32_t)moe::f32_to_bf16_rne(a0) | ((uint32_t)moe::f32_to_bf16_rne(a1) << 16);

@@ -94,6 +94,7 @@ struct DecArgs {
     int pass_rows;              // activation rows staged per pass
     int ldx;                    // staged row stride, fp16 elements
     int extra;                  // block rows for passes beyond each expert's first
+    int single_token;           // gate+up with T == 1: every routed row is token 0
 };
 
 // 8 E2M1 codes (one 32-bit word: k .. k+7) times the block scale, as fp16.
@@ -160,10 +161,19 @@ __device__ __forceinline__ void put_f16x8(uint16_t *dst, const f32x4_t &a, const
 // values: the first and the last lane's rows get one atomic each after a wave
 // reduction; lanes of any row strictly between (short rows only) post their
 // own.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Wave maximum: DPP within each 16-lane row, then the four row results.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    return v;
+    v = max(v, dpp_u32<moe::kDppXor1>(v));
+    v = max(v, dpp_u32<moe::kDppXor2>(v));
+    v = max(v, dpp_u32<moe::kDppHalfMirror>(v));
+    v = max(v, dpp_u32<moe::kDppMirror>(v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
 }
 __device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v) {
     const int lane = threadIdx.x & 63;
@@ -210,7 +220,8 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                 const int m = ic[i] / cpr, kc = ic[i] - m * cpr;
                 const uint4 v = uint4{raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
                 *reinterpret_cast<uint4 *>(xs + m * ldx + 8 * kc) = v;
-                row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
+                if (base + i * kThreads < nch)  // uniform: the sub-batch holds real chunks
+                    row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
             }
         };
         // The first batch is peeled so that mid() sits on a single path.
@@ -254,7 +265,8 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
             }
             mid();
 #pragma unroll
-            for (int i = 0; i < SB; ++i) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+            for (int i = 0; i < SB; ++i)
+                if (i * kThreads < nch) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
             __syncthreads();  // maxima complete
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
@@ -279,7 +291,8 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                 }
                 if constexpr (decltype(first)::value) mid();
 #pragma unroll
-                for (int i = 0; i < SB; ++i) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+                for (int i = 0; i < SB; ++i)
+                    if (base + i * kThreads < nch) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
             };
             batch(0, std::true_type{});
             for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
@@ -378,23 +391,38 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     };
 
     if (threadIdx.x < 16) rmax[threadIdx.x] = 0u;
+    // Activation rows whose addresses need no lookup (down: h by position;
+    // gate+up with one token: x row 0) are loaded before the ring, so waiting
+    // for them waits for no weight.  Otherwise the lookup of the pass's tokens
+    // goes first, then ring slot 0, then the x rows, then the rest of the
+    // ring: the x rows wait for slot 0 only, and while they are converted the
+    // rest of the ring is in flight.
+    const bool x_first = !GATED || a.single_token;
     int tokv = 0;  // gate+up: token of row (lane & 15) of the pass
-    if constexpr (GATED) tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    if (!x_first) tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
     __syncthreads();  // rmax cleared
-    // The first ring slot, then the activation loads, then the rest of the
-    // ring: the activations wait only for slot 0, and while they are
-    // converted the rest of the ring is in flight.
     __builtin_amdgcn_sched_barrier(0);
-    load(0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
-        __builtin_amdgcn_sched_barrier(0);
+    if (x_first) {
+        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int d = 1; d < D; ++d) {
-            load(d);
-            __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-        }
-    });
+            for (int d = 0; d < D; ++d) {
+                load(d);
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+            }
+        });
+    } else {
+        load(0);
+        __builtin_amdgcn_sched_barrier(0);
+        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 1; d < D; ++d) {
+                load(d);
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+            }
+        });
+    }
 
     const int TG = (pr + 3) >> 2;
     const int tA = n >> 2, cA = n & 3;  // A-operand role: token tA of each group, quarter cA
@@ -749,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
 // Shapes: N % 64 == 0, K % 64 == 0 and K >= 256 (checked by the callers).
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
-                          const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
+                          const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
                           hipStream_t stream) {
     DecArgs a;
     a.act = act;
@@ -766,6 +794,7 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.out = out;
     a.N = N;
     a.K = K;
+    a.single_token = gated && T == 1;
     const int ucols = gated ? 16 : 32;
     a.units = (N + ucols - 1) / ucols;
     const int cap = E < P ? E : P;

@@ -135,6 +135,101 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
     for (int p = total + tid; p < P; p += kSortThreads) sorted_tok[p] = -1;
 }
 
+// Few pairs (P <= 64): one pair per lane of wave 0, one LDS histogram, no
+// second read of the ids.  Same results as k_moe_sort.
+constexpr int kSmallThreads = 256;
+constexpr int kSmallPairs = 64;
+
+__global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
+    const int32_t *__restrict__ ids, int P, int k, int E, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_tok, int32_t *__restrict__ pair_pos, int32_t *__restrict__ active,
+    int32_t *__restrict__ active_count, uint32_t *__restrict__ err_flag) {
+    __shared__ int cnt[MOE_NVFP4_MAX_EXPERTS];
+    __shared__ int wsum[2][kSmallThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = tid < P ? ids[tid] : -1;
+    const bool valid = tid < P && e >= 0 && e < E;
+    for (int i = tid; i < E; i += kSmallThreads) cnt[i] = 0;
+    if (wave == 0 && __ballot(tid < P && !valid) != 0ull && lane == 0)
+        atomicOr(err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
+    __syncthreads();
+    if (valid) atomicAdd(&cnt[e], 1);
+    __syncthreads();
+
+    // Exclusive scans over the experts (4 consecutive per thread) of the
+    // counts and of the active flags.
+    int c[4], s0 = 0, s1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ex = 4 * tid + i;
+        c[i] = ex < E ? cnt[ex] : 0;
+        s0 += c[i];
+        s1 += c[i] > 0 ? 1 : 0;
+    }
+    int i0 = s0, i1 = s1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o0 = __shfl_up(i0, d, 64), o1 = __shfl_up(i1, d, 64);
+        if (lane >= d) {
+            i0 += o0;
+            i1 += o1;
+        }
+    }
+    if (lane == 63) {
+        wsum[0][wave] = i0;
+        wsum[1][wave] = i1;
+    }
+    __syncthreads();
+    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+        if (w < wave) {
+            b0 += wsum[0][w];
+            b1 += wsum[1][w];
+        }
+        t0 += wsum[0][w];
+        t1 += wsum[1][w];
+    }
+    int off = b0 + i0 - s0, aidx = b1 + i1 - s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ex = 4 * tid + i;
+        if (ex < E) {
+            offsets[ex] = off;
+            cnt[ex] = off;  // base of the expert's positions, read by the ranking below
+            if (c[i] > 0) active[aidx++] = ex;
+            if (ex >= t1) active[ex] = -1;
+        }
+        off += c[i];
+    }
+    if (tid == 0) {
+        offsets[E] = t0;
+        *active_count = t1;
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        // Stable rank among equal ids: lanes are in flat pair order.
+        int rank = 0;
+        unsigned long long rem = __ballot(valid);
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        while (rem) {
+            const int leader = __ffsll((long long)rem) - 1;
+            const int v = __builtin_amdgcn_readlane(e, leader);
+            const bool mine = valid && e == v;
+            const unsigned long long m = __ballot(mine);
+            if (mine) rank = __popcll(m & lt);
+            rem &= ~m;
+        }
+        if (tid < P) {
+            const int pos = valid ? cnt[e] + rank : -1;
+            pair_pos[tid] = pos;
+            if (valid) sorted_tok[pos] = tid / k;
+        }
+    }
+    for (int p = t0 + tid; p < P; p += kSmallThreads) sorted_tok[p] = -1;
+}
+
 }  // namespace
 
 extern "C" int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
@@ -147,6 +242,11 @@ extern "C" int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int
     if (T < 1 || k < 1 || E < 1 || k > E) return MOE_NVFP4_ESHAPE;
     if (E > MOE_NVFP4_MAX_EXPERTS || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
     const int P = T * k;
+    if (P <= kSmallPairs) {
+        hipLaunchKernelGGL(k_moe_sort_small, dim3(1), dim3(kSmallThreads), 0, (hipStream_t)stream, topk_ids, P, k,
+                           E, expert_offsets, sorted_token_ids, pair_pos, active_experts, active_count, err_flag);
+        return moe_host::launch_status();
+    }
     const size_t lds = (size_t)kSortWaves * E * sizeof(int);
     hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), lds, (hipStream_t)stream, topk_ids, P,
                        k, E, expert_offsets, sorted_token_ids, pair_pos, active_experts, active_count,
