@@ -255,13 +255,14 @@ def test_kmajor_matches_rowmajor_on_same_weights():
     parity.assert_parity(ob, ref["out"], "K-major")
 
 
-def test_row_major_activation_range():
+@pytest.mark.parametrize("kmajor", [False, True])
+def test_activation_range(kmajor):
     """Token rows scaled by 2^40, 2^-40 and 2^60 (beyond fp16's range either
-    way): the decode path stages each row with its own power-of-two factor,
-    so every row of h, y and out follows the oracle at its own magnitude
-    (scale-invariant rules, row by row)."""
-    say("activation range, row-major")
-    shape = synth.MoeShape("range", 6, 512, 384, 4, 2, "uniform", False)
+    way): the decode path stages each row with its own power-of-two factor and
+    the many-token path computes in bf16, so every row of h, y and out follows
+    the oracle at its own magnitude (scale-invariant rules, row by row)."""
+    say("activation range", "kmajor" if kmajor else "row-major")
+    shape = synth.MoeShape("range", 6, 512, 384, 4, 2, "uniform", kmajor)
     case = Case(16, shape)
     bits = case.x_bits.astype(np.uint32)
     shift = {1: 40, 2: -40, 4: 60}  # h of the 2^60 row is near 2^108, inside fp32
@@ -283,11 +284,20 @@ def test_row_major_activation_range():
         parity.assert_parity_relative(out[t], ref["out"][t], f"out row {t}")
 
 
+@pytest.mark.parametrize("kmajor", [False, True])
 @pytest.mark.parametrize("routing", ["uniform", "zipf"])
-def test_row_major_many_experts_and_passes(routing):
+def test_many_experts_and_passes(routing, kmajor):
     """64 experts, 800 routed rows: several units per block, and with
     Zipf-skewed routing experts whose rows take several passes on extra
-    block rows."""
-    say("many experts and passes", routing)
-    shape = synth.MoeShape(f"wide_{routing}", 200, 768, 1024, 64, 4, routing, False)
-    _full_check(Case(17, shape), f"wide {routing}")
+    block rows (row-major) or several row tiles (K-major)."""
+    say("many experts and passes", routing, "kmajor" if kmajor else "row-major")
+    shape = synth.MoeShape(f"wide_{routing}", 200, 768, 1024, 64, 4, routing, kmajor)
+    _full_check(Case(17, shape), f"wide {routing} {kmajor}")
+
+
+def test_kmajor_few_experts_many_rows():
+    """4 experts, 700 tokens, top-2: about 350 rows per expert, so every
+    expert is split into several balanced row tiles in both projections."""
+    say("K-major, few experts with many rows")
+    shape = synth.MoeShape("tall", 700, 512, 640, 4, 2, "uniform", True)
+    _full_check(Case(18, shape), "tall kmajor")
