@@ -18,20 +18,24 @@
 //     columns are interleaved by 4.  Lane (c = lane%16, q = lane/16) owns
 //     columns 4c..4c+3 of the wave's 64 and k-octet q of each 32-k step.
 //   * Each wave owns 64 weight columns and all rows of the block tile (up to
-//     160 = 10 MFMA row tiles), so every weight element is decoded once per
-//     block and reused by every row tile; the 4 waves share the activation
-//     tile, staged through LDS as bf16 (one barrier per 32-k step, two
-//     buffers).  Gate+up: waves 0/1 hold gate columns, waves 2/3 the same up
-//     columns; the up accumulators reach the gate waves through LDS in the
-//     epilogue.
-//   * An expert's rows are split into ceil(rows/160) balanced tiles.  Blocks
-//     are dealt to the 8 XCDs in contiguous ranges of (row tile, column tile)
-//     units, column tile fastest, so the blocks that share an activation tile
-//     run on one XCD together; the ranges are cut from the true unit count,
-//     read on the device, so every XCD gets an equal share.
-//   * Weight dwords are prefetched kBDist steps ahead in registers, ring
+//     144 rows = 9 MFMA row tiles for gate+up, 128 for down), so every weight
+//     element is decoded once per block and reused by every row tile; the 4
+//     waves share the activation tile, staged through LDS as bf16 with one
+//     barrier per 32-k step.  Gate+up: waves 0/1 hold gate columns, waves 2/3
+//     the same up columns; the up accumulators reach the gate waves through
+//     LDS in the epilogue.
+//   * Gate+up stages x with direct global-to-LDS loads three steps ahead
+//     (no registers); down converts fp32 h to bf16 in registers one step
+//     ahead.
+//   * An expert's rows are split into balanced tiles.  Blocks are dealt to
+//     the 8 XCDs in contiguous ranges of (row tile, column tile) units,
+//     column tile fastest, so the blocks that share an activation tile run on
+//     one XCD together; the ranges are cut from the true unit count, read on
+//     the device, so every XCD gets an equal share.
+//   * Weight dwords are prefetched kBDist steps ahead in registers; ring
 //     refills are unconditional (clamped to the last step) so the compiler
-//     keeps them in flight across iterations.
+//     keeps them in flight across iterations.  Within a step the next step's
+//     weights are decoded between this step's MFMAs.
 #include <type_traits>
 
 #include "moe_common.hpp"
@@ -53,15 +57,46 @@ constexpr int kExRows = 48;                      // epilogue exchange: rows per 
 // Rows per block tile.  Down stages fp32 h through registers (twice the
 // registers of the bf16 x chunks), so its tile is two MFMA row tiles shorter
 // to stay within 256 registers at two waves per SIMD.
+//
+// Gate+up stages x with direct global-to-LDS loads (no registers) into a ring
+// of kAStages buffers of unpadded 64-byte rows whose 16-byte octets are
+// XOR-swizzled by row (conflict-free operand reads); down converts fp32 h to
+// bf16 in registers and stages it into two padded buffers.
 template <bool GATED>
 struct Tile {
-    static constexpr int kMaxRows = GATED ? 160 : 128;
+    static constexpr int kMaxRows = GATED ? 144 : 128;
     static constexpr int kMT = kMaxRows / 16;                        // MFMA row tiles
-    static constexpr int kStage = kMaxRows * kRowBytes;              // one activation buffer
+    static constexpr int kRow = GATED ? 64 : kRowBytes;              // LDS bytes per staged row
+    static constexpr int kAStages = GATED ? 4 : 2;
+    static constexpr int kStage = kMaxRows * kRow;                   // one activation buffer
     static constexpr int kChunks = kMaxRows * 4;                     // 16-byte (8 k) chunks per step
     static constexpr int kSlots = (kChunks + kThreads - 1) / kThreads;
+    static constexpr int kDma = kChunks / 64;                        // wave-wide direct loads per step
 };
-static_assert(kExRows * 128 * 4 <= 2 * Tile<true>::kStage, "exchange fits in the activation buffers");
+static_assert(Tile<true>::kChunks % 64 == 0, "whole wave-wide direct loads");
+
+// s_waitcnt immediate that waits until at most n vector-memory loads of this
+// wave are outstanding (vmcnt in bits 3:0 and 15:14; LDS/scalar and export
+// counters left at their maxima, i.e. not waited for).
+constexpr int waitcnt_vm(int n) { return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15); }
+
+// Workgroup barrier without the release fence of __syncthreads: that fence
+// would wait for every outstanding load (the direct loads into LDS count as
+// outstanding stores), emptying the prefetch ring at every step.  The caller
+// waits for the direct loads the other waves need by count; LDS reads and
+// writes of this wave are complete once their results were used or their
+// counter was waited for, which the compiler does before the MFMAs that use
+// them and the asm fences keep memory operations on their side.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Swizzle of the 16-byte octet of staged row r: conflict-free operand reads
+// whether the LDS serves 16 lanes x 16 bytes per cycle (64 banks) or 8 lanes
+// (32 banks).
+__device__ __forceinline__ int octet_swizzle(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 static_assert(kExRows % 16 == 0, "exchange rounds cover whole row tiles");
 
 struct GemmArgs {
@@ -81,29 +116,60 @@ struct GemmArgs {
     int n_ct;      // column tiles
 };
 
-// Decode 4 packed dwords (rows k/2 .. k/2+3 of columns 4c..4c+3) and their
-// 4 E4M3 scales into the B operands of the 4 interleaved column tiles.
-__device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf16x8_t (&b)[4]) {
-    const float sc[4] = {moe::e4m3_f32<0>(s), moe::e4m3_f32<1>(s), moe::e4m3_f32<2>(s), moe::e4m3_f32<3>(s)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[r], 1.0f, 0) * sc[0];
-        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[r], 1.0f, 1) * sc[1];
-        const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[r], 1.0f, 2) * sc[2];
-        const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[r], 1.0f, 3) * sc[3];
-        const bf16x2_t p0 = __builtin_convertvector(v0, bf16x2_t);
-        const bf16x2_t p1 = __builtin_convertvector(v1, bf16x2_t);
-        const bf16x2_t p2 = __builtin_convertvector(v2, bf16x2_t);
-        const bf16x2_t p3 = __builtin_convertvector(v3, bf16x2_t);
-        b[0][2 * r] = p0.x;
-        b[0][2 * r + 1] = p0.y;
-        b[1][2 * r] = p1.x;
-        b[1][2 * r + 1] = p1.y;
-        b[2][2 * r] = p2.x;
-        b[2][2 * r + 1] = p2.y;
-        b[3][2 * r] = p3.x;
-        b[3][2 * r + 1] = p3.y;
+// E4M3 block scales of the 4 columns in a scale dword.
+struct Scales4 {
+    float v[4];
+};
+__device__ __forceinline__ Scales4 scales4(uint32_t s) {
+    return Scales4{{moe::e4m3_f32<0>(s), moe::e4m3_f32<1>(s), moe::e4m3_f32<2>(s), moe::e4m3_f32<3>(s)}};
+}
+
+// Decode packed row r (one dword: columns 4c..4c+3, k pair 2r, 2r+1 of the
+// lane's octet) into element pair r of the B operands of the 4 interleaved
+// column tiles.
+__device__ __forceinline__ void decode_row(uint32_t w, const Scales4 &sc, int r, bf16x8_t (&b)[4]) {
+    const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc.v[0];
+    const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * sc.v[1];
+    const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2) * sc.v[2];
+    const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3) * sc.v[3];
+    const bf16x2_t p0 = __builtin_convertvector(v0, bf16x2_t);
+    const bf16x2_t p1 = __builtin_convertvector(v1, bf16x2_t);
+    const bf16x2_t p2 = __builtin_convertvector(v2, bf16x2_t);
+    const bf16x2_t p3 = __builtin_convertvector(v3, bf16x2_t);
+    b[0][2 * r] = p0.x;
+    b[0][2 * r + 1] = p0.y;
+    b[1][2 * r] = p1.x;
+    b[1][2 * r + 1] = p1.y;
+    b[2][2 * r] = p2.x;
+    b[2][2 * r + 1] = p2.y;
+    b[3][2 * r] = p3.x;
+    b[3][2 * r + 1] = p3.y;
+}
+
+// One element pair u = 4r + j: packed row r, column 4c+j (byte j).  Called
+// from fully unrolled loops, where u folds to a constant.
+template <int J>
+__device__ __forceinline__ bf16x2_t decode_pair(uint32_t w, float sc) {
+    return __builtin_convertvector(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J) * sc, bf16x2_t);
+}
+__device__ __forceinline__ void decode_pair_at(int u, const uint32_t (&w)[4], const Scales4 &sc, bf16x8_t (&b)[4]) {
+    const int r = u >> 2, j = u & 3;
+    bf16x2_t pr;
+    switch (j) {
+        case 0: pr = decode_pair<0>(w[r], sc.v[0]); break;
+        case 1: pr = decode_pair<1>(w[r], sc.v[1]); break;
+        case 2: pr = decode_pair<2>(w[r], sc.v[2]); break;
+        default: pr = decode_pair<3>(w[r], sc.v[3]); break;
     }
+    b[j][2 * r] = pr.x;
+    b[j][2 * r + 1] = pr.y;
+}
+
+// All 4 packed rows of a step (8 consecutive k of columns 4c..4c+3).
+__device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf16x8_t (&b)[4]) {
+    const Scales4 sc = scales4(s);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) decode_row(w[r], sc, r, b);
 }
 
 __device__ __forceinline__ u32x4_t f32x8_to_bf16x8(u32x4_t a, u32x4_t b) {
@@ -122,8 +188,10 @@ __device__ __forceinline__ u32x4_t f32x8_to_bf16x8(u32x4_t a, u32x4_t b) {
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_kmajor(GemmArgs a) {
     constexpr int kMaxRows = Tile<GATED>::kMaxRows, kMT = Tile<GATED>::kMT, kStage = Tile<GATED>::kStage;
-    constexpr int kChunks = Tile<GATED>::kChunks, kSlots = Tile<GATED>::kSlots;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+    constexpr int kChunks = Tile<GATED>::kChunks, kSlots = Tile<GATED>::kSlots, kRow = Tile<GATED>::kRow;
+    constexpr int kAStages = Tile<GATED>::kAStages;
+    constexpr int kLds = GATED && kExRows * 128 * 4 > kAStages * kStage ? kExRows * 128 * 4 : kAStages * kStage;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
     auto tiles_of = [](int rows) { return (rows + kMaxRows - 1) / kMaxRows; };
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -209,53 +277,78 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint8_t *pk = up_wave ? pB : pA;
     const uint8_t *sk = up_wave ? a.sb[e] : a.sa[e];
     const int n_ld = wact ? n_w : N - 64;  // idle waves (N not a multiple of the tile) read valid columns
-    const uint8_t *bp = pk + (size_t)(4 * q) * N + n_ld + 4 * c;
-    const uint8_t *sp = sk + (size_t)(q >> 1) * N + n_ld + 4 * c;
+    // Per-lane byte offsets (32-bit) from wave-uniform bases, so that loads
+    // take the scalar-base + vector-offset form.
+    const uint32_t boff = (uint32_t)(4 * q) * N + n_ld + 4 * c;
+    const uint32_t soff = (uint32_t)(q >> 1) * N + n_ld + 4 * c;
 
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
 
     // ---- activation staging: chunk = 8 k of one row ----------------------
-    const void *asrc[kSlots];
+    // Byte offsets of each chunk in x (gate+up, gathered by token) or in h
+    // (down, sorted order); the host bounds both tensors below 4 GiB.
+    const uint8_t *abytes = static_cast<const uint8_t *>(a.act);
+    // Gate+up: direct loads.  Wave w issues load slots g = w, w+4, w+8, ...
+    // (g < kDma); lane l of slot g writes LDS bytes [16 (64 g + l), +16),
+    // i.e. staged row (64 g + l) / 4 and physical octet l % 4, so it fetches
+    // the logical octet that the swizzle places there.
+    constexpr int kDma = Tile<GATED>::kDma;
+    constexpr int kDmaPerWave = (kDma + 3) / 4;
+    uint32_t doff[kDmaPerWave];
+    // Down: register staging, chunk slots j (thread tid + 256 j).
+    uint32_t aoff[kSlots];
     int adst[kSlots];
+    if constexpr (GATED) {
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-        const int ch = tid + kThreads * j;
-        const int row = ch >> 2, oct = ch & 3;
-        const int rr = row < mrows ? row : 0;
-        if constexpr (GATED)
-            asrc[j] = static_cast<const uint16_t *>(a.act) + (size_t)a.sorted_tok[row0 + rr] * K + 8 * oct;
-        else
-            asrc[j] = static_cast<const float *>(a.act) + (row0 + rr) * K + 8 * oct;
-        adst[j] = row * kRowBytes + 16 * oct;
+        for (int t = 0; t < kDmaPerWave; ++t) {
+            const int g = wave + 4 * t < kDma ? wave + 4 * t : kDma - 1;
+            const int u = 64 * g + lane;
+            const int row = u >> 2, oct = (u & 3) ^ octet_swizzle(row);
+            const int rr = row < mrows ? row : 0;
+            doff[t] = ((uint32_t)a.sorted_tok[row0 + rr] * (uint32_t)K + 8 * oct) * 2u;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            const int ch = tid + kThreads * j;
+            const int row = ch >> 2, oct = ch & 3;
+            const int rr = row < mrows ? row : 0;
+            aoff[j] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8 * oct) * 4u;
+            adst[j] = row * kRow + 16 * oct;
+        }
     }
+    // Gate+up: issue step s into ring buffer st (clamped past the last step).
+    auto dma_a = [&](int s, int st) {
+        const int sc_ = s < S ? s : S - 1;
+        const uint8_t *base = abytes + (size_t)sc_ * kBK * 2;
+#pragma unroll
+        for (int t = 0; t < kDmaPerWave; ++t) {
+            if (t < kDmaPerWave - 1 || wave + 4 * t < kDma) {
+                const int g = wave + 4 * t;
+                __builtin_amdgcn_global_load_lds(
+                    (const MOE_GLOBAL void *)(base + doff[t]),
+                    (__attribute__((address_space(3))) void *)(lds + st * kStage + 1024 * g), 16, 0, 0);
+            }
+        }
+    };
     // (kChunks need not fill the last slot: slot j is live for tid < kChunks - kThreads*j.)
-    u32x4_t ar[kSlots][GATED ? 1 : 2];
+    u32x4_t ar[kSlots][2];
     auto load_a = [&](int s) {
+        const uint8_t *base = abytes + (size_t)s * kBK * 4;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j) {
             if (kThreads * j + kThreads <= kChunks || tid < kChunks - kThreads * j) {
-                if constexpr (GATED) {
-                    ar[j][0] = gload<u32x4_t>(static_cast<const uint16_t *>(asrc[j]) + kBK * s);
-                } else {
-                    const float *p = static_cast<const float *>(asrc[j]) + kBK * s;
-                    ar[j][0] = gload<u32x4_t>(p);
-                    ar[j][1] = gload<u32x4_t>(p + 4);
-                }
+                ar[j][0] = gload<u32x4_t>(base + aoff[j]);
+                ar[j][1] = gload<u32x4_t>(base + aoff[j] + 16);
             }
         }
     };
     auto store_a = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < kSlots; ++j) {
-            if (kThreads * j + kThreads <= kChunks || tid < kChunks - kThreads * j) {
-                u32x4_t v;
-                if constexpr (GATED)
-                    v = ar[j][0];
-                else
-                    v = f32x8_to_bf16x8(ar[j][0], ar[j][1]);
-                *reinterpret_cast<u32x4_t *>(lds + buf * kStage + adst[j]) = v;
-            }
+            if (kThreads * j + kThreads <= kChunks || tid < kChunks - kThreads * j)
+                *reinterpret_cast<u32x4_t *>(lds + buf * kStage + adst[j]) = f32x8_to_bf16x8(ar[j][0], ar[j][1]);
         }
     };
 
@@ -264,10 +357,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     uint32_t bs[kBDist];
     auto load_b = [&](int slot_s, uint32_t (&w)[4], uint32_t &sv) {
         const int s = slot_s < S ? slot_s : S - 1;
-        const uint8_t *p = bp + (size_t)(16 * s) * N;
+        const uint8_t *p = pk + (size_t)(16 * s) * N;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = gload<uint32_t>(p + (size_t)r * N);
-        sv = gload<uint32_t>(sp + (size_t)(2 * s) * N);
+        for (int r = 0; r < 4; ++r) w[r] = gload<uint32_t>(p + (size_t)r * N + boff);
+        sv = gload<uint32_t>(sk + (size_t)(2 * s) * N + soff);
     };
 
     f32x4_t acc[kMT][4];
@@ -276,47 +369,126 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // B operands of the current step and of the next one (decoded while the
+    // current step's MFMAs run).
+    bf16x8_t bop[2][4];
 #pragma unroll
     for (int d = 0; d < kBDist; ++d) load_b(d, bw[d], bs[d]);
-    load_a(0);
-    store_a(0);
-    __syncthreads();
+    decode_b(bw[0], bs[0], bop[0]);
+    load_b(kBDist, bw[0], bs[0]);
+    if constexpr (GATED) {
+        static_assert(kAStages == 4 && kBDist == 4, "the wait counts below assume these depths");
+        dma_a(0, 0);
+        dma_a(1, 1);
+        dma_a(2, 2);
+        // Direct loads are waited for by count.  Step 0's landed once at
+        // most the newer ones (steps 1 and 2: 2 or 3 loads each) are
+        // outstanding; counting 2 per step is exact for waves 1-3 and
+        // stricter than needed for wave 0.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        block_barrier();
+    } else {
+        load_a(0);
+        store_a(0);
+        __syncthreads();
+    }
 
-    const uint8_t *abase = lds + c * kRowBytes + 16 * q;
+    // Lane's operand offset in a staged buffer: row c of each 16-row tile, octet q.
+    const uint8_t *abase = GATED ? lds + c * kRow + 16 * (q ^ octet_swizzle(c)) : lds + c * kRow + 16 * q;
 
+    // Step s: slot s % kBDist of the ring was decoded into bop[s % 2] during
+    // step s - 1; this step decodes step s + 1 and refills its slot with step
+    // s + 1 + kBDist.  Every row tile runs (rows past the tile's end compute
+    // values that are never stored), so one basic block holds the MFMAs, the
+    // pipelined operand reads and the decode, and the scheduler can
+    // interleave them.
     auto step = [&](int s, auto slot) {
         constexpr int d = decltype(slot)::value;
-        const int buf = s & 1;
+        constexpr int p = d & 1;
+        constexpr int dn = (d + 1) % kBDist;
         const bool more = s + 1 < S;
-        if (more) load_a(s + 1);
-        bf16x8_t bop[4];
-        decode_b(bw[d], bs[d], bop);
-        load_b(s + kBDist, bw[d], bs[d]);
-        const uint8_t *ab = abase + buf * kStage;
+        constexpr int st = GATED ? d % kAStages : p;  // buffer read by this step
+        if constexpr (GATED)
+            dma_a(s + 3, (d + 3) % kAStages);
+        else if (more)
+            load_a(s + 1);
+        const uint8_t *ab = abase + st * kStage;
+        const Scales4 scn = scales4(bs[dn]);
+        // Hand-ordered: row-tile operands are read two tiles ahead, and one
+        // element pair of the next step's decode (4 VALU) follows every other
+        // MFMA, so that it issues in the matrix pipe's shadow.  Full
+        // scheduling fences keep this order; the empty asm after each decoded
+        // pair pins it there (otherwise it is sunk to its use in the next
+        // step).
+        bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab);
+        bf16x8_t an = *reinterpret_cast<const bf16x8_t *>(ab + 16 * kRow);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
-            if (i < mt_used) {
-                const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab + i * 16 * kRowBytes);
+            const bf16x8_t an2 = *reinterpret_cast<const bf16x8_t *>(ab + (i + 2 < kMT ? i + 2 : kMT - 1) * 16 * kRow);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[p][j], acc[i][j], 0, 0, 0);
+                const int m = 4 * i + j;  // MFMA index in the step
+                if ((m & 1) == 0 && m / 2 < 16) {
+                    decode_pair_at(m / 2, bw[dn], scn, bop[p ^ 1]);
+                    asm volatile("" : "+v"(bop[p ^ 1][0]), "+v"(bop[p ^ 1][1]), "+v"(bop[p ^ 1][2]), "+v"(bop[p ^ 1][3]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
+            av = an;
+            an = an2;
         }
-        if (more) store_a(buf ^ 1);
-        __syncthreads();
+        load_b(s + 1 + kBDist, bw[dn], bs[dn]);
+        if constexpr (GATED) {
+            // Step s + 1's direct loads must have landed before the barrier.
+            // Loads issued after them (2 direct loads per step, 5 per
+            // refill; the prologue issued steps 0-2 after its refill):
+            //   s = 0:  step 2, then step 3 + refill            = 2 + 2 + 5
+            //   s = 1:  steps 3, 4 and two refills              = 2 * (2 + 5)
+            //   s >= 2: the refill after them, then two steps   = 5 + 2 * (2 + 5)
+            if (s == 0)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+            else if (s == 1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(19));
+            block_barrier();
+        } else {
+            if (more) store_a(p ^ 1);
+            __syncthreads();
+        }
     };
 
+    // The step loop is unrolled by the ring depth so that ring slots, B
+    // operand parity and activation buffer are compile-time indices.
+    static_assert(kBDist == 2 || kBDist == 4, "ring depth");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     int s0 = 0;
     for (; s0 + kBDist <= S; s0 += kBDist) {
-        step(s0 + 0, std::integral_constant<int, 0>{});
-        step(s0 + 1, std::integral_constant<int, 1>{});
-        step(s0 + 2, std::integral_constant<int, 2>{});
-        step(s0 + 3, std::integral_constant<int, 3>{});
+        step(s0 + 0, I0{});
+        step(s0 + 1, I1{});
+        if constexpr (kBDist == 4) {
+            step(s0 + 2, I2{});
+            step(s0 + 3, I3{});
+        }
     }
-    static_assert(kBDist == 4, "the step loop is unrolled by the ring depth");
-    if (s0 + 0 < S) step(s0 + 0, std::integral_constant<int, 0>{});
-    if (s0 + 1 < S) step(s0 + 1, std::integral_constant<int, 1>{});
-    if (s0 + 2 < S) step(s0 + 2, std::integral_constant<int, 2>{});
+    if (s0 + 0 < S) step(s0 + 0, I0{});
+    if constexpr (kBDist == 4) {
+        if (s0 + 1 < S) step(s0 + 1, I1{});
+        if (s0 + 2 < S) step(s0 + 2, I2{});
+    }
+
+    if constexpr (GATED) {
+        // The last steps issued direct loads past the end (clamped repeats
+        // that keep the wait counts uniform); drain them before the epilogue
+        // reuses the buffers.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        block_barrier();
+    }
 
     // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j] ----
     float *out = a.out;
