@@ -137,9 +137,12 @@ int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
  *                     active expert are left untouched.
  * Admission: H % 64 == 0 and I % 64 == 0 (both layouts), H >= 256 and
  * I >= 256 (ROW_MAJOR); packed, scale and activation buffers 16-byte
- * aligned.  The K_MAJOR path feeds the matrix cores with fp16
- * operands, so it admits activations of magnitude below 65504.
- * Errors: ENULL, ESHAPE, ELAYOUT, ELIMIT (E, P or width above the maxima).
+ * aligned; K_MAJOR: the activation tensor (x here, h for the down
+ * projection) below 4 GiB.  The K_MAJOR path feeds the matrix cores with
+ * bf16 operands (x as given, the decoded weights exactly), so it admits the
+ * whole bf16 range.
+ * Errors: ENULL, ESHAPE, ELAYOUT, ELIMIT (E, P or width above the maxima,
+ * or a K_MAJOR activation tensor of 4 GiB or more).
  */
 int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
                            int32_t I, moe_nvfp4_experts gate, moe_nvfp4_experts up,

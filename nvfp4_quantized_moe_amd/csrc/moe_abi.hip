@@ -44,6 +44,7 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
     if (gate.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
                                      gate, &up, h, I, H, T, P, E, (hipStream_t)stream);
+    if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
                                   &up, h, I, H, P, E, (hipStream_t)stream);
 }
@@ -60,6 +61,7 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
     if (down.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
                                      nullptr, y, H, I, T, P, E, (hipStream_t)stream);
+    if ((uint64_t)P * I * 4 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(false, h, nullptr, expert_offsets, active_experts, active_count, down,
                                   nullptr, y, H, I, P, E, (hipStream_t)stream);
 }

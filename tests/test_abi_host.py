@@ -57,6 +57,8 @@ def test_gate_up_rejects():
     assert call(I=528, g=_ex(1), u=_ex(1)) == ESHAPE    # K-major needs I % 64 == 0
     assert call(k=5) == ESHAPE
     assert call(H=1 << 17) == ELIMIT
+    # K-major: x of 4 GiB or more (activation offsets are 32-bit)
+    assert call(T=1 << 16, H=1 << 15, g=_ex(1), u=_ex(1)) == ELIMIT
 
 
 def test_down_and_blend_and_transpose_reject():
@@ -64,6 +66,8 @@ def test_down_and_blend_and_transpose_reject():
     assert L.moe_nvfp4_down(None, 4, 2, 4, 256, 512, _ex(), D, D, D, D, None) == ENULL
     assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 512, _ex(null=True), D, D, D, D, None) == ENULL
     assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 500, _ex(), D, D, D, D, None) == ESHAPE
+    # K-major: h of 4 GiB or more
+    assert L.moe_nvfp4_down(D, 1 << 20, 4, 4, 256, 1024, _ex(1), D, D, D, D, None) == ELIMIT
     assert L.moe_nvfp4_blend(D, D, None, 4, 2, 256, D, None) == ENULL
     assert L.moe_nvfp4_blend(D, D, D, 0, 2, 256, D, None) == ESHAPE
     assert L.moe_nvfp4_blend(D, D, D, 4, 2, 1 << 17, D, None) == ELIMIT
