@@ -12,12 +12,27 @@
 //           among equal ids in the same 64 is found with ballots, so ranks
 //           follow the flat index; the last lane of each id advances the base.
 // No global atomics touch the ordering, so the output is deterministic.
+// Lanes holding equal ids are found by one ballot per bit of the id
+// (ceil(log2 E) ballots per 64 pairs, whatever the number of distinct ids).
 #include "moe_common.hpp"
 
 namespace {
 
+// Mask of the lanes whose id equals this lane's (among lanes with valid set),
+// from one ballot per id bit.
+__device__ __forceinline__ unsigned long long match_lanes(int e, bool valid, int nbits) {
+    unsigned long long eq = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long m = __ballot(valid && bit);
+        eq &= bit ? m : ~m;
+    }
+    return eq;
+}
+
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / moe::kWave;
+constexpr int kIdsPerLane = 8;
 
 // Exclusive scan of one int per thread over the whole 1024-thread block.
 __device__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
@@ -64,13 +79,34 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
     const int f1 = min(P, f0 + per_wave);
     int *my = cnt + wave * E;
 
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    // The slice is read kIdsPerLane chunks of 64 at a time, all loads of a
+    // group issued together; a slice of one group stays in registers for
+    // pass 2.
+    const int ngroups = (f1 - f0 + 64 * kIdsPerLane - 1) / (64 * kIdsPerLane);
+    int ev[kIdsPerLane];
+    auto load_group = [&](int g) {
+#pragma unroll
+        for (int j = 0; j < kIdsPerLane; ++j) {
+            const int f = f0 + 64 * (kIdsPerLane * g + j) + lane;
+            ev[j] = f < f1 ? ids[f] : -1;
+        }
+    };
     bool bad = false;
-    for (int f = f0 + lane; f < f1; f += 64) {
-        int e = ids[f];
-        if (e >= 0 && e < E)
-            atomicAdd(&my[e], 1);
-        else
-            bad = true;
+    for (int g = 0; g < ngroups; ++g) {
+        load_group(g);
+#pragma unroll
+        for (int j = 0; j < kIdsPerLane; ++j) {
+            const int f = f0 + 64 * (kIdsPerLane * g + j) + lane;
+            if (f - lane >= f1) break;  // uniform: past the slice
+            const int e = ev[j];
+            const bool valid = f < f1 && e >= 0 && e < E;
+            bad |= f < f1 && !valid;
+            // The first lane of each id adds the group's count.
+            const unsigned long long eq = match_lanes(e, valid, nbits);
+            if (valid && (eq & lt) == 0ull) my[e] += __popcll(eq);
+        }
     }
     if (__ballot(bad) != 0ull && lane == 0) atomicOr(err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
     __syncthreads();
@@ -103,33 +139,26 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
     __syncthreads();
 
     // Pass 2: stable positions.
-    for (int base = f0; base < f1; base += 64) {
-        const int f = base + lane;
-        const bool in = f < f1;
-        const int e = in ? ids[f] : -1;
-        const bool valid = in && e >= 0 && e < E;
-        int rank = 0, same = 0;
-        unsigned long long rem = __ballot(valid);
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        while (rem) {
-            const int leader = __ffsll((long long)rem) - 1;
-            const int v = __builtin_amdgcn_readlane(e, leader);
-            const bool mine = valid && e == v;
-            const unsigned long long m = __ballot(mine);
-            if (mine) {
-                rank = __popcll(m & lt);
-                same = __popcll(m);
+    for (int g = 0; g < ngroups; ++g) {
+        if (ngroups > 1) load_group(g);
+#pragma unroll
+        for (int j = 0; j < kIdsPerLane; ++j) {
+            const int f = f0 + 64 * (kIdsPerLane * g + j) + lane;
+            if (f - lane >= f1) break;  // uniform: past the slice
+            const bool in = f < f1;
+            const int e = ev[j];
+            const bool valid = in && e >= 0 && e < E;
+            const unsigned long long eq = match_lanes(e, valid, nbits);
+            const int rank = __popcll(eq & lt), same = __popcll(eq);
+            int pos = -1;
+            if (valid) pos = my[e] + rank;
+            // All lanes of this wave have read their base before any lane
+            // writes it (LDS operations of one wave complete in order).
+            if (valid && rank == same - 1) my[e] = pos + 1;
+            if (in) {
+                pair_pos[f] = pos;
+                if (valid) sorted_tok[pos] = f / k;
             }
-            rem &= ~m;
-        }
-        int pos = -1;
-        if (valid) pos = my[e] + rank;
-        // All lanes of this wave have read their base before any lane writes it
-        // (LDS operations of one wave complete in order).
-        if (valid && rank == same - 1) my[e] = pos + 1;
-        if (in) {
-            pair_pos[f] = pos;
-            if (valid) sorted_tok[pos] = f / k;
         }
     }
     for (int p = total + tid; p < P; p += kSortThreads) sorted_tok[p] = -1;
@@ -210,17 +239,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
 
     if (wave == 0) {
         // Stable rank among equal ids: lanes are in flat pair order.
-        int rank = 0;
-        unsigned long long rem = __ballot(valid);
         const unsigned long long lt = (1ull << lane) - 1ull;
-        while (rem) {
-            const int leader = __ffsll((long long)rem) - 1;
-            const int v = __builtin_amdgcn_readlane(e, leader);
-            const bool mine = valid && e == v;
-            const unsigned long long m = __ballot(mine);
-            if (mine) rank = __popcll(m & lt);
-            rem &= ~m;
-        }
+        const int rank = __popcll(match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
         if (tid < P) {
             const int pos = valid ? cnt[e] + rank : -1;
             pair_pos[tid] = pos;

@@ -86,7 +86,8 @@ def test_sort_configs_bit_exact(cfg):
 
 @pytest.mark.parametrize("T,k,E,mode", [(1, 1, 1, "rand"), (3, 4, 5, "dup"), (9, 3, 7, "invalid"),
                                          (16384, 8, 256, "rand"), (2048, 4, 1024, "rand"), (512, 1, 1024, "skew"),
-                                         (100, 8, 8, "all_same")])
+                                         (100, 8, 8, "all_same"), (1000, 3, 50, "rand"),
+                                         (5000, 7, 300, "invalid")])
 def test_sort_edge_cases_bit_exact(T, k, E, mode):
     say("sort edge", T, k, E, mode)
     rng = np.random.default_rng(T * 31 + k * 7 + E)
