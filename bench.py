@@ -17,7 +17,7 @@ instead).  Reported on one JSON line:
   roofline    the dominant kernel (gate+up+SiLU): its algorithmic bytes per
               launch / its mean launch duration, timed with HIP events on the
               stream it runs on, against 8 TB/s (the many-token K-major
-              workload: its flops per launch against the 2.5 PFLOP/s fp16
+              workload: its flops per launch against the 2.5 PFLOP/s bf16/fp16
               matrix-core peak); traffic = HBM bytes per launch from the
               committed counter summary in profiles/ while the kernel sources
               are unchanged since it was taken, else null
