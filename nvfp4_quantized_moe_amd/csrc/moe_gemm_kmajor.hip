@@ -11,31 +11,30 @@
 //     decoded weights the B operand, fp32 accumulation.  bf16 holds every
 //     E2M1 x E4M3 product exactly (at most 6 significant bits) and x as given;
 //     h is rounded to bf16 when staged for the down projection.
-//   * The weights never pass through LDS.  In the K-major layout one dword
-//     at packed row k/2 covers 4 adjacent columns x 2 k, so a lane that loads
-//     the dwords of 4 consecutive packed rows holds 8 consecutive k of 4
-//     columns: exactly the B operand (8 k of one column) of 4 MFMAs whose
-//     columns are interleaved by 4.  Lane (c = lane%16, q = lane/16) owns
-//     columns 4c..4c+3 of the wave's 64 and k-octet q of each 32-k step.
-//   * Each wave owns 64 weight columns and all rows of the block tile (up to
-//     144 rows = 9 MFMA row tiles for gate+up, 128 for down), so every weight
-//     element is decoded once per block and reused by every row tile; the 4
-//     waves share the activation tile, staged through LDS as bf16 with one
-//     barrier per 32-k step.  Gate+up: waves 0/1 hold gate columns, waves 2/3
-//     the same up columns; the up accumulators reach the gate waves through
-//     LDS in the epilogue.
-//   * Gate+up stages x with direct global-to-LDS loads three steps ahead
-//     (no registers); down converts fp32 h to bf16 in registers one step
-//     ahead.
+//   * In the K-major layout one dword at packed row k/2 covers 4 adjacent
+//     columns x 2 k, so a lane holding the dwords of 4 consecutive packed rows
+//     holds 8 consecutive k of 4 columns: exactly the B operand (8 k of one
+//     column) of 4 MFMAs whose columns are interleaved by 4.  Lane
+//     (c = lane%16, q = lane/16) owns columns 4c..4c+3 of its wave's 64 and
+//     k-octet q of each 32-k step; decoding needs no cross-lane traffic.
+//   * Each wave owns 64 weight columns and every row of the block tile, so
+//     every weight element is decoded once per block and reused by every row
+//     tile; the 4 waves share the activation tile, staged in LDS as bf16 with
+//     one barrier per 32-k step.
+//   * Gate+up (k_gemm_gate_up, up to 144 rows): waves 0/1 hold 128 gate
+//     columns, waves 2/3 the same up columns, and the up accumulators reach
+//     the gate waves through LDS for silu(g) * u.  x and the weights move
+//     with direct global-to-LDS loads three steps ahead, so no registers hold
+//     data in flight; each wave decodes its step's weights from LDS.
+//   * Down (k_gemm_down, up to 128 rows, 256 output columns per block):
+//     fp32 h is converted to bf16 in registers one step ahead; the weights
+//     stream through a register ring four steps deep, and the next step's
+//     weights are decoded between this step's MFMAs.
 //   * An expert's rows are split into balanced tiles.  Blocks are dealt to
 //     the 8 XCDs in contiguous ranges of (row tile, column tile) units,
 //     column tile fastest, so the blocks that share an activation tile run on
 //     one XCD together; the ranges are cut from the true unit count, read on
 //     the device, so every XCD gets an equal share.
-//   * Weight dwords are prefetched kBDist steps ahead in registers; ring
-//     refills are unconditional (clamped to the last step) so the compiler
-//     keeps them in flight across iterations.  Within a step the next step's
-//     weights are decoded between this step's MFMAs.
 #include <type_traits>
 
 #include "moe_common.hpp"
@@ -47,57 +46,15 @@ using moe::u32x4_t;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+#define MOE_LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;                          // k per step
-constexpr int kRowBytes = 80;                    // LDS bytes per staged row: 32 bf16 + 16 padding
-constexpr int kBDist = 4;                        // weight prefetch distance, in steps
-constexpr int kExRows = 48;                      // epilogue exchange: rows per round
-
-// Rows per block tile.  Down stages fp32 h through registers (twice the
-// registers of the bf16 x chunks), so its tile is two MFMA row tiles shorter
-// to stay within 256 registers at two waves per SIMD.
-//
-// Gate+up stages x with direct global-to-LDS loads (no registers) into a ring
-// of kAStages buffers of unpadded 64-byte rows whose 16-byte octets are
-// XOR-swizzled by row (conflict-free operand reads); down converts fp32 h to
-// bf16 in registers and stages it into two padded buffers.
-template <bool GATED>
-struct Tile {
-    static constexpr int kMaxRows = GATED ? 144 : 128;
-    static constexpr int kMT = kMaxRows / 16;                        // MFMA row tiles
-    static constexpr int kRow = GATED ? 64 : kRowBytes;              // LDS bytes per staged row
-    static constexpr int kAStages = GATED ? 4 : 2;
-    static constexpr int kStage = kMaxRows * kRow;                   // one activation buffer
-    static constexpr int kChunks = kMaxRows * 4;                     // 16-byte (8 k) chunks per step
-    static constexpr int kSlots = (kChunks + kThreads - 1) / kThreads;
-    static constexpr int kDma = kChunks / 64;                        // wave-wide direct loads per step
-};
-static_assert(Tile<true>::kChunks % 64 == 0, "whole wave-wide direct loads");
-
-// s_waitcnt immediate that waits until at most n vector-memory loads of this
-// wave are outstanding (vmcnt in bits 3:0 and 15:14; LDS/scalar and export
-// counters left at their maxima, i.e. not waited for).
-constexpr int waitcnt_vm(int n) { return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15); }
-
-// Workgroup barrier without the release fence of __syncthreads: that fence
-// would wait for every outstanding load (the direct loads into LDS count as
-// outstanding stores), emptying the prefetch ring at every step.  The caller
-// waits for the direct loads the other waves need by count; LDS reads and
-// writes of this wave are complete once their results were used or their
-// counter was waited for, which the compiler does before the MFMAs that use
-// them and the asm fences keep memory operations on their side.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Swizzle of the 16-byte octet of staged row r: conflict-free operand reads
-// whether the LDS serves 16 lanes x 16 bytes per cycle (64 banks) or 8 lanes
-// (32 banks).
-__device__ __forceinline__ int octet_swizzle(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-static_assert(kExRows % 16 == 0, "exchange rounds cover whole row tiles");
+constexpr int kBK = 32;     // k per step
+constexpr int kBDist = 4;   // weight prefetch depth, in steps (ring stages)
+using I0 = std::integral_constant<int, 0>;
+using I1 = std::integral_constant<int, 1>;
+using I2 = std::integral_constant<int, 2>;
+using I3 = std::integral_constant<int, 3>;
 
 struct GemmArgs {
     const void *act;              // gate+up: bf16 x [T, K]; down: fp32 h [P, K]
@@ -116,34 +73,17 @@ struct GemmArgs {
     int n_ct;      // column tiles
 };
 
-// E4M3 block scales of the 4 columns in a scale dword.
+// ---------------------------------------------------------------------------
+// Weight decode: E2M1 pairs through the f32 converter (scale 1: the hardware
+// applies only the scale's exponent), times the E4M3 block scale in f32, then
+// rounded to bf16 (exact: at most 6 significant bits).
+// ---------------------------------------------------------------------------
 struct Scales4 {
     float v[4];
 };
+// E4M3 block scales of the 4 columns in a scale dword.
 __device__ __forceinline__ Scales4 scales4(uint32_t s) {
     return Scales4{{moe::e4m3_f32<0>(s), moe::e4m3_f32<1>(s), moe::e4m3_f32<2>(s), moe::e4m3_f32<3>(s)}};
-}
-
-// Decode packed row r (one dword: columns 4c..4c+3, k pair 2r, 2r+1 of the
-// lane's octet) into element pair r of the B operands of the 4 interleaved
-// column tiles.
-__device__ __forceinline__ void decode_row(uint32_t w, const Scales4 &sc, int r, bf16x8_t (&b)[4]) {
-    const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc.v[0];
-    const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * sc.v[1];
-    const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2) * sc.v[2];
-    const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3) * sc.v[3];
-    const bf16x2_t p0 = __builtin_convertvector(v0, bf16x2_t);
-    const bf16x2_t p1 = __builtin_convertvector(v1, bf16x2_t);
-    const bf16x2_t p2 = __builtin_convertvector(v2, bf16x2_t);
-    const bf16x2_t p3 = __builtin_convertvector(v3, bf16x2_t);
-    b[0][2 * r] = p0.x;
-    b[0][2 * r + 1] = p0.y;
-    b[1][2 * r] = p1.x;
-    b[1][2 * r + 1] = p1.y;
-    b[2][2 * r] = p2.x;
-    b[2][2 * r + 1] = p2.y;
-    b[3][2 * r] = p3.x;
-    b[3][2 * r + 1] = p3.y;
 }
 
 // One element pair u = 4r + j: packed row r, column 4c+j (byte j).  Called
@@ -165,11 +105,25 @@ __device__ __forceinline__ void decode_pair_at(int u, const uint32_t (&w)[4], co
     b[j][2 * r + 1] = pr.y;
 }
 
-// All 4 packed rows of a step (8 consecutive k of columns 4c..4c+3).
+// All 4 packed rows of a step (8 consecutive k of columns 4c..4c+3) into the
+// B operands of the 4 interleaved column tiles.
 __device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf16x8_t (&b)[4]) {
     const Scales4 sc = scales4(s);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) decode_row(w[r], sc, r, b);
+    for (int r = 0; r < 4; ++r) {
+        const bf16x2_t p0 = decode_pair<0>(w[r], sc.v[0]);
+        const bf16x2_t p1 = decode_pair<1>(w[r], sc.v[1]);
+        const bf16x2_t p2 = decode_pair<2>(w[r], sc.v[2]);
+        const bf16x2_t p3 = decode_pair<3>(w[r], sc.v[3]);
+        b[0][2 * r] = p0.x;
+        b[0][2 * r + 1] = p0.y;
+        b[1][2 * r] = p1.x;
+        b[1][2 * r + 1] = p1.y;
+        b[2][2 * r] = p2.x;
+        b[2][2 * r + 1] = p2.y;
+        b[3][2 * r] = p3.x;
+        b[3][2 * r + 1] = p3.y;
+    }
 }
 
 __device__ __forceinline__ u32x4_t f32x8_to_bf16x8(u32x4_t a, u32x4_t b) {
@@ -185,19 +139,42 @@ __device__ __forceinline__ u32x4_t f32x8_to_bf16x8(u32x4_t a, u32x4_t b) {
     return r;
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_kmajor(GemmArgs a) {
-    constexpr int kMaxRows = Tile<GATED>::kMaxRows, kMT = Tile<GATED>::kMT, kStage = Tile<GATED>::kStage;
-    constexpr int kChunks = Tile<GATED>::kChunks, kSlots = Tile<GATED>::kSlots, kRow = Tile<GATED>::kRow;
-    constexpr int kAStages = Tile<GATED>::kAStages;
-    constexpr int kLds = GATED && kExRows * 128 * 4 > kAStages * kStage ? kExRows * 128 * 4 : kAStages * kStage;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+// s_waitcnt immediate that waits until at most n vector-memory loads of this
+// wave are outstanding (vmcnt in bits 3:0 and 15:14; LDS/scalar and export
+// counters left at their maxima, i.e. not waited for).
+constexpr int waitcnt_vm(int n) { return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15); }
+
+// Workgroup barrier without the release fence of __syncthreads: that fence
+// would wait for every outstanding load (direct loads into LDS count as
+// outstanding stores), emptying the prefetch rings at every step.  Callers
+// wait for the direct loads the other waves need by count; this wave's LDS
+// writes are waited for here, and the asm fences keep memory operations on
+// their side.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Swizzle of the 16-byte octet of staged row r: conflict-free operand reads
+// whether the LDS serves 16 lanes x 16 bytes per cycle (64 banks) or 8 lanes
+// (32 banks).
+__device__ __forceinline__ int octet_swizzle(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// ---------------------------------------------------------------------------
+// Work split: the block's (row tile, column tile) unit.
+// ---------------------------------------------------------------------------
+struct Unit {
+    int e, lo, m0, mrows, ct;
+};
+
+// Row tiles per expert: ceil(rows / kMaxRows), balanced.  Units are dealt to
+// the XCDs in contiguous ranges (blocks go to XCDs round-robin).  Returns
+// false, the same on every wave, if the block has no unit.
+template <int kMaxRows>
+__device__ bool find_unit(const GemmArgs &a, Unit &u) {
+    const int lane = threadIdx.x & 63;
     auto tiles_of = [](int rows) { return (rows + kMaxRows - 1) / kMaxRows; };
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = moe::wave_id();
-
-    // ---- which unit: count the row tiles, then cut per-XCD ranges --------
     const int nact = *a.nactive;
     int total = 0;
     for (int base = 0; base < nact; base += 64) {
@@ -215,8 +192,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int per_xcd = (units + 7) >> 3;
     const int local = blockIdx.x >> 3;
     const int unit = (blockIdx.x & 7) * per_xcd + local;
-    if (local >= per_xcd || unit >= units) return;  // uniform exit
-    const int mt = unit / a.n_ct, ct = unit - mt * a.n_ct;
+    if (local >= per_xcd || unit >= units) return false;
+    const int mt = unit / a.n_ct;
+    const int ct = unit - mt * a.n_ct;
 
     int e = -1, lo = 0, m0 = 0, mrows = 0;
     int seen = 0;
@@ -250,109 +228,318 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         seen += __shfl(incl, 63, 64);
     }
-    e = __builtin_amdgcn_readfirstlane(e);
-    if (e < 0) return;  // uniform
-    lo = __builtin_amdgcn_readfirstlane(lo);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    mrows = __builtin_amdgcn_readfirstlane(mrows);
+    u.e = __builtin_amdgcn_readfirstlane(e);
+    u.lo = __builtin_amdgcn_readfirstlane(lo);
+    u.m0 = __builtin_amdgcn_readfirstlane(m0);
+    u.mrows = __builtin_amdgcn_readfirstlane(mrows);
+    u.ct = __builtin_amdgcn_readfirstlane(ct);
+    return u.e >= 0;
+}
 
+// Rows of an absent (NULL) expert are written as zeros.
+__device__ void zero_rows(const GemmArgs &a, size_t row0, int mrows, int n0, int cols) {
+    for (int i = threadIdx.x; i < mrows * cols; i += kThreads) {
+        const int r = i / cols, cc = n0 + (i - r * cols);
+        if (cc < a.N) a.out[(row0 + r) * a.N + cc] = 0.f;
+    }
+}
+
+// ===========================================================================
+// Gate+up.
+// ===========================================================================
+constexpr int kRowsG = 144;                  // rows per block tile
+constexpr int kMTG = kRowsG / 16;            // MFMA row tiles
+constexpr int kStageG = kRowsG * 64;         // activation buffer: unpadded 64-byte rows, swizzled octets
+constexpr int kDmaG = kRowsG * 4 / 64;       // wave-wide direct loads per activation step
+constexpr int kDmaPerWaveG = (kDmaG + 3) / 4;
+constexpr int kWStage = 4 * 1024 + 4 * 256;  // weight stage: 4 waves x (1 KiB packed), 4 x 256 B scales
+constexpr int kExRows = 16;                  // epilogue exchange: rows per round
+static_assert(kRowsG * 4 % 64 == 0, "whole wave-wide direct loads");
+static_assert(kExRows * 128 * 4 <= kStageG, "exchange fits in one activation buffer");
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_gate_up(GemmArgs a) {
+    // One LDS array per ring stage: alias analysis then tells the compiler's
+    // wait insertion which direct loads an LDS read depends on (with one
+    // array it would wait for all of them).  Activations sa*, weights sw*:
+    // per wave 1 KiB of packed bytes (16 packed rows x 64 columns), then per
+    // wave 256 bytes of scales (2 rows x 64 columns, stored twice).
+    __shared__ __attribute__((aligned(16))) uint8_t sa0[kStageG], sa1[kStageG], sa2[kStageG], sa3[kStageG];
+    __shared__ __attribute__((aligned(16))) uint8_t sw0[kWStage], sw1[kWStage], sw2[kWStage], sw3[kWStage];
+    auto abuf = [&](auto st) -> uint8_t * {
+        constexpr int v = decltype(st)::value;
+        if constexpr (v == 0) return sa0;
+        else if constexpr (v == 1) return sa1;
+        else if constexpr (v == 2) return sa2;
+        else return sa3;
+    };
+    auto wbuf = [&](auto st) -> uint8_t * {
+        constexpr int v = decltype(st)::value;
+        if constexpr (v == 0) return sw0;
+        else if constexpr (v == 1) return sw1;
+        else if constexpr (v == 2) return sw2;
+        else return sw3;
+    };
+
+    Unit un;
+    if (!find_unit<kRowsG>(a, un)) return;  // uniform exit
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::wave_id();
     const int N = a.N, K = a.K;
     const int c = lane & 15, q = lane >> 4;
-    const int n0 = ct * (GATED ? 128 : 256);
-    const int n_w = n0 + 64 * (GATED ? (wave & 1) : wave);  // this wave's first weight column
+    const int e = un.e, mrows = un.mrows;
+    const int n0 = un.ct * 128;
+    const int n_w = n0 + 64 * (wave & 1);  // this wave's first weight column
     const bool wact = n_w < N;
-    const size_t row0 = (size_t)lo + m0;
+    const size_t row0 = (size_t)un.lo + un.m0;
 
     const uint8_t *pA = a.pa[e];
-    const uint8_t *pB = GATED ? a.pb[e] : pA;
-    if (pA == nullptr || pB == nullptr) {  // absent expert: its rows are zero
-        const int cols = GATED ? 128 : 256;
-        for (int i = tid; i < mrows * cols; i += kThreads) {
-            const int r = i / cols, cc = n0 + (i - r * cols);
-            if (cc < N) a.out[(row0 + r) * N + cc] = 0.f;
-        }
+    const uint8_t *pB = a.pb[e];
+    if (pA == nullptr || pB == nullptr) {
+        zero_rows(a, row0, mrows, n0, 128);
         return;
     }
-    const bool up_wave = GATED && wave >= 2;
+    const bool up_wave = wave >= 2;
     const uint8_t *pk = up_wave ? pB : pA;
     const uint8_t *sk = up_wave ? a.sb[e] : a.sa[e];
-    const int n_ld = wact ? n_w : N - 64;  // idle waves (N not a multiple of the tile) read valid columns
-    // Per-lane byte offsets (32-bit) from wave-uniform bases, so that loads
-    // take the scalar-base + vector-offset form.
-    const uint32_t boff = (uint32_t)(4 * q) * N + n_ld + 4 * c;
-    const uint32_t soff = (uint32_t)(q >> 1) * N + n_ld + 4 * c;
-
+    const int n_ld = wact ? n_w : N - 64;  // idle waves (N not a multiple of 128) read valid columns
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
 
-    // ---- activation staging: chunk = 8 k of one row ----------------------
-    // Byte offsets of each chunk in x (gate+up, gathered by token) or in h
-    // (down, sorted order); the host bounds both tensors below 4 GiB.
-    const uint8_t *abytes = static_cast<const uint8_t *>(a.act);
-    // Gate+up: direct loads.  Wave w issues load slots g = w, w+4, w+8, ...
-    // (g < kDma); lane l of slot g writes LDS bytes [16 (64 g + l), +16),
-    // i.e. staged row (64 g + l) / 4 and physical octet l % 4, so it fetches
-    // the logical octet that the swizzle places there.
-    constexpr int kDma = Tile<GATED>::kDma;
-    constexpr int kDmaPerWave = (kDma + 3) / 4;
-    uint32_t doff[kDmaPerWave];
-    // Down: register staging, chunk slots j (thread tid + 256 j).
-    uint32_t aoff[kSlots];
-    int adst[kSlots];
-    if constexpr (GATED) {
+    // ---- activations: direct loads of x rows gathered by token ---------
+    // Wave w issues load slots g = w, w+4, w+8 (g < kDmaG); lane l of slot g
+    // writes LDS bytes [16 (64 g + l), +16), i.e. staged row (64 g + l) / 4
+    // and physical octet l % 4, so it fetches the logical octet that the
+    // swizzle places there.  Offsets are 32-bit (x below 4 GiB).
+    const uint8_t *xbytes = static_cast<const uint8_t *>(a.act);
+    uint32_t doff[kDmaPerWaveG];
 #pragma unroll
-        for (int t = 0; t < kDmaPerWave; ++t) {
-            const int g = wave + 4 * t < kDma ? wave + 4 * t : kDma - 1;
-            const int u = 64 * g + lane;
-            const int row = u >> 2, oct = (u & 3) ^ octet_swizzle(row);
-            const int rr = row < mrows ? row : 0;
-            doff[t] = ((uint32_t)a.sorted_tok[row0 + rr] * (uint32_t)K + 8 * oct) * 2u;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-            const int ch = tid + kThreads * j;
-            const int row = ch >> 2, oct = ch & 3;
-            const int rr = row < mrows ? row : 0;
-            aoff[j] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8 * oct) * 4u;
-            adst[j] = row * kRow + 16 * oct;
-        }
+    for (int t = 0; t < kDmaPerWaveG; ++t) {
+        const int g = wave + 4 * t < kDmaG ? wave + 4 * t : kDmaG - 1;
+        const int u = 64 * g + lane;
+        const int row = u >> 2, oct = (u & 3) ^ octet_swizzle(row);
+        const int rr = row < mrows ? row : 0;
+        doff[t] = ((uint32_t)a.sorted_tok[row0 + rr] * (uint32_t)K + 8 * oct) * 2u;
     }
-    // Gate+up: issue step s into ring buffer st (clamped past the last step).
-    auto dma_a = [&](int s, int st) {
+    auto dma_a = [&](int s, auto st) {  // step s (clamped past the end) into buffer st
         const int sc_ = s < S ? s : S - 1;
-        const uint8_t *base = abytes + (size_t)sc_ * kBK * 2;
+        const uint8_t *base = xbytes + (size_t)sc_ * kBK * 2;
 #pragma unroll
-        for (int t = 0; t < kDmaPerWave; ++t) {
-            if (t < kDmaPerWave - 1 || wave + 4 * t < kDma) {
-                const int g = wave + 4 * t;
-                __builtin_amdgcn_global_load_lds(
-                    (const MOE_GLOBAL void *)(base + doff[t]),
-                    (__attribute__((address_space(3))) void *)(lds + st * kStage + 1024 * g), 16, 0, 0);
-            }
+        for (int t = 0; t < kDmaPerWaveG; ++t) {
+            if (t < kDmaPerWaveG - 1 || wave + 4 * t < kDmaG)
+                __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(base + doff[t]),
+                                                 (MOE_LDS void *)(abuf(st) + 1024 * (wave + 4 * t)), 16, 0, 0);
         }
     };
-    // (kChunks need not fill the last slot: slot j is live for tid < kChunks - kThreads*j.)
-    u32x4_t ar[kSlots][2];
-    auto load_a = [&](int s) {
-        const uint8_t *base = abytes + (size_t)s * kBK * 4;
+
+    // ---- weights: direct loads of this wave's 64 columns ----------------
+    // Only the loading wave reads them back.  Packed: lane l loads 16 bytes
+    // (16 columns) of packed row 16 s + 4 (t & 3) + (t >> 2), t = l >> 2,
+    // chunk l & 3; it lands at byte 16 l, so row 4 q + r of the step sits at
+    // byte 256 r + 64 q and the dword of columns 4c..4c+3 at + 4c: a lane's
+    // four rows are 256 bytes apart and each read of 64 lanes touches 64
+    // distinct banks.  Scales: lane l (mod 32) loads the dword of row
+    // (l >> 4) & 1, columns 4 (l & 15) .. +3.
+    const int bt = lane >> 2;
+    const uint32_t bdoff = (uint32_t)(4 * (bt & 3) + (bt >> 2)) * N + n_ld + 16 * (lane & 3);
+    const uint32_t sdoff = (uint32_t)((lane >> 4) & 1) * N + n_ld + 4 * (lane & 15);
+    auto dma_b = [&](int s, auto st) {
+        const int sc_ = s < S ? s : S - 1;
+        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(pk + (size_t)(16 * sc_) * N + bdoff),
+                                         (MOE_LDS void *)(wbuf(st) + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(sk + (size_t)(2 * sc_) * N + sdoff),
+                                         (MOE_LDS void *)(wbuf(st) + 4096 + wave * 256), 4, 0, 0);
+    };
+    const int brd = wave * 1024 + 64 * q + 4 * c, srd = 4096 + wave * 256 + 4 * (16 * (q >> 1) + c);
+    auto read_b = [&](auto st, uint32_t (&w)[4], uint32_t &sv) {
+        const uint8_t *b = wbuf(st) + brd;
 #pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-            if (kThreads * j + kThreads <= kChunks || tid < kChunks - kThreads * j) {
-                ar[j][0] = gload<u32x4_t>(base + aoff[j]);
-                ar[j][1] = gload<u32x4_t>(base + aoff[j] + 16);
+        for (int r = 0; r < 4; ++r) w[r] = *reinterpret_cast<const uint32_t *>(b + 256 * r);
+        sv = *reinterpret_cast<const uint32_t *>(wbuf(st) + srd);
+    };
+
+    f32x4_t acc[kMTG][4];
+#pragma unroll
+    for (int i = 0; i < kMTG; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t bop[4];
+    uint32_t bw[4], bsv;
+
+    // Every step issues, per wave, 2 activation direct loads (3 on wave 0)
+    // and 2 weight loads, three steps ahead.  Before the barrier that ends
+    // step s, step s + 1's loads must have landed: issued two steps back, so
+    // at most 2 * (2 + 2) = 8 newer loads (stricter than needed on wave 0).
+    // Decoding the next step's weights between this step's MFMAs (as the
+    // down kernel does) measured slower here: the second set of B operands
+    // costs 16 registers this kernel does not have.
+    static_assert(kBDist == 4, "four ring stages");
+    dma_a(0, I0{});
+    dma_b(0, I0{});
+    dma_a(1, I1{});
+    dma_b(1, I1{});
+    dma_a(2, I2{});
+    dma_b(2, I2{});
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+    block_barrier();
+
+    // Lane's operand offset in a staged buffer: row c of each 16-row tile, octet q.
+    const int aoffs = c * 64 + 16 * (q ^ octet_swizzle(c));
+
+    // Step s: issue step s + 3, decode this step's weights, run every row
+    // tile (rows past the tile's end compute values that are never stored),
+    // then wait for step s + 1 and meet at the barrier.
+    auto step = [&](int s, auto slot) {
+        constexpr int d = decltype(slot)::value;
+        using Sn = std::integral_constant<int, (d + 3) % kBDist>;
+        dma_a(s + 3, Sn{});
+        dma_b(s + 3, Sn{});
+        read_b(slot, bw, bsv);
+        decode_b(bw, bsv, bop);
+        const uint8_t *ab = abuf(slot) + aoffs;
+        // Row-tile operands are read two tiles ahead.
+        bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab);
+        bf16x8_t an = *reinterpret_cast<const bf16x8_t *>(ab + 1024);
+#pragma unroll
+        for (int i = 0; i < kMTG; ++i) {
+            const bf16x8_t an2 = *reinterpret_cast<const bf16x8_t *>(ab + (i + 2 < kMTG ? i + 2 : kMTG - 1) * 1024);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[j], acc[i][j], 0, 0, 0);
+            av = an;
+            an = an2;
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+        block_barrier();
+    };
+    int s0 = 0;
+    for (; s0 + kBDist <= S; s0 += kBDist) {
+        step(s0 + 0, I0{});
+        step(s0 + 1, I1{});
+        step(s0 + 2, I2{});
+        step(s0 + 3, I3{});
+    }
+    if (s0 + 0 < S) step(s0 + 0, I0{});
+    if (s0 + 1 < S) step(s0 + 1, I1{});
+    if (s0 + 2 < S) step(s0 + 2, I2{});
+
+    // The last steps issued loads past the end (clamped repeats that keep the
+    // wait counts uniform); drain them before the exchange reuses sa0.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_barrier();
+
+    // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j].
+    // Up waves hand u = s2u * acc to the gate waves through LDS.
+    const float s2g = a.s2a[e], s2u = a.s2b[e];
+    float *ex = reinterpret_cast<float *>(sa0);
+    const int exc = 64 * (wave & 1) + 4 * c;  // column within the block's 128
+    constexpr int kExTiles = kExRows / 16;
+#pragma unroll
+    for (int i0 = 0; i0 < kMTG; i0 += kExTiles) {
+        if (i0 < mt_used) {
+            if (up_wave) {
+#pragma unroll
+                for (int i = i0; i < i0 + kExTiles && i < kMTG; ++i) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int rl = 16 * (i - i0) + 4 * q + v;
+                        *reinterpret_cast<float4 *>(ex + rl * 128 + exc) =
+                            make_float4(acc[i][0][v] * s2u, acc[i][1][v] * s2u, acc[i][2][v] * s2u,
+                                        acc[i][3][v] * s2u);
+                    }
+                }
             }
+            __syncthreads();
+            if (!up_wave && wact) {
+#pragma unroll
+                for (int i = i0; i < i0 + kExTiles && i < kMTG; ++i) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int rl = 16 * (i - i0) + 4 * q + v;
+                        const int row = 16 * i + 4 * q + v;
+                        if (row < mrows) {
+                            const float4 u = *reinterpret_cast<const float4 *>(ex + rl * 128 + exc);
+                            float4 o;
+                            o.x = moe::silu_f32(acc[i][0][v] * s2g) * u.x;
+                            o.y = moe::silu_f32(acc[i][1][v] * s2g) * u.y;
+                            o.z = moe::silu_f32(acc[i][2][v] * s2g) * u.z;
+                            o.w = moe::silu_f32(acc[i][3][v] * s2g) * u.w;
+                            *reinterpret_cast<float4 *>(a.out + (row0 + row) * N + n_w + 4 * c) = o;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ===========================================================================
+// Down.
+// ===========================================================================
+constexpr int kRowsD = 128;                // rows per block tile
+constexpr int kMTD = kRowsD / 16;
+constexpr int kRowD = 80;                  // LDS bytes per staged row: 32 bf16 + 16 padding
+constexpr int kStageD = kRowsD * kRowD;
+constexpr int kChunksD = kRowsD * 4;       // 16-byte (8 k) chunks per step
+constexpr int kSlotsD = kChunksD / kThreads;
+static_assert(kChunksD % kThreads == 0, "whole chunk slots");
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_down(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageD];
+
+    Unit un;
+    if (!find_unit<kRowsD>(a, un)) return;  // uniform exit
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = moe::wave_id();
+    const int N = a.N, K = a.K;
+    const int c = lane & 15, q = lane >> 4;
+    const int e = un.e, mrows = un.mrows;
+    const int n0 = un.ct * 256;
+    const int n_w = n0 + 64 * wave;
+    const bool wact = n_w < N;
+    const size_t row0 = (size_t)un.lo + un.m0;
+
+    const uint8_t *pk = a.pa[e];
+    if (pk == nullptr) {
+        zero_rows(a, row0, mrows, n0, 256);
+        return;
+    }
+    const uint8_t *sk = a.sa[e];
+    const int n_ld = wact ? n_w : N - 64;
+    // Per-lane byte offsets (32-bit) from wave-uniform bases.
+    const uint32_t boff = (uint32_t)(4 * q) * N + n_ld + 4 * c;
+    const uint32_t soff = (uint32_t)(q >> 1) * N + n_ld + 4 * c;
+    const int S = K / kBK;
+    const int mt_used = (mrows + 15) >> 4;
+
+    // ---- activations: fp32 h rows -> bf16, register staging one step ahead.
+    const uint8_t *hbytes = static_cast<const uint8_t *>(a.act);
+    uint32_t aoff[kSlotsD];
+    int adst[kSlotsD];
+#pragma unroll
+    for (int j = 0; j < kSlotsD; ++j) {
+        const int ch = tid + kThreads * j;
+        const int row = ch >> 2, oct = ch & 3;
+        const int rr = row < mrows ? row : 0;
+        aoff[j] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8 * oct) * 4u;  // h below 4 GiB
+        adst[j] = row * kRowD + 16 * oct;
+    }
+    u32x4_t ar[kSlotsD][2];
+    auto load_a = [&](int s) {
+        const uint8_t *base = hbytes + (size_t)s * kBK * 4;
+#pragma unroll
+        for (int j = 0; j < kSlotsD; ++j) {
+            ar[j][0] = gload<u32x4_t>(base + aoff[j]);
+            ar[j][1] = gload<u32x4_t>(base + aoff[j] + 16);
         }
     };
     auto store_a = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-            if (kThreads * j + kThreads <= kChunks || tid < kChunks - kThreads * j)
-                *reinterpret_cast<u32x4_t *>(lds + buf * kStage + adst[j]) = f32x8_to_bf16x8(ar[j][0], ar[j][1]);
-        }
+        for (int j = 0; j < kSlotsD; ++j)
+            *reinterpret_cast<u32x4_t *>(lds + buf * kStageD + adst[j]) = f32x8_to_bf16x8(ar[j][0], ar[j][1]);
     };
 
-    // ---- weight ring --------------------------------------------------------
+    // ---- weight ring in registers ---------------------------------------
     uint32_t bw[kBDist][4];
     uint32_t bs[kBDist];
     auto load_b = [&](int slot_s, uint32_t (&w)[4], uint32_t &sv) {
@@ -363,9 +550,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         sv = gload<uint32_t>(sk + (size_t)(2 * s) * N + soff);
     };
 
-    f32x4_t acc[kMT][4];
+    f32x4_t acc[kMTD][4];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMTD; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -374,57 +561,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     bf16x8_t bop[2][4];
 #pragma unroll
     for (int d = 0; d < kBDist; ++d) load_b(d, bw[d], bs[d]);
+    load_a(0);
+    store_a(0);
     decode_b(bw[0], bs[0], bop[0]);
     load_b(kBDist, bw[0], bs[0]);
-    if constexpr (GATED) {
-        static_assert(kAStages == 4 && kBDist == 4, "the wait counts below assume these depths");
-        dma_a(0, 0);
-        dma_a(1, 1);
-        dma_a(2, 2);
-        // Direct loads are waited for by count.  Step 0's landed once at
-        // most the newer ones (steps 1 and 2: 2 or 3 loads each) are
-        // outstanding; counting 2 per step is exact for waves 1-3 and
-        // stricter than needed for wave 0.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-        block_barrier();
-    } else {
-        load_a(0);
-        store_a(0);
-        __syncthreads();
-    }
+    __syncthreads();
 
-    // Lane's operand offset in a staged buffer: row c of each 16-row tile, octet q.
-    const uint8_t *abase = GATED ? lds + c * kRow + 16 * (q ^ octet_swizzle(c)) : lds + c * kRow + 16 * q;
+    const uint8_t *abase = lds + c * kRowD + 16 * q;
 
-    // Step s: slot s % kBDist of the ring was decoded into bop[s % 2] during
-    // step s - 1; this step decodes step s + 1 and refills its slot with step
-    // s + 1 + kBDist.  Every row tile runs (rows past the tile's end compute
-    // values that are never stored), so one basic block holds the MFMAs, the
-    // pipelined operand reads and the decode, and the scheduler can
-    // interleave them.
+    // Step s: ring slot s % kBDist was decoded into bop[s % 2] during step
+    // s - 1; this step decodes step s + 1 and refills its slot with step
+    // s + 1 + kBDist (unconditionally, clamped: the compiler then keeps the
+    // ring in flight across iterations).  Every row tile runs.
     auto step = [&](int s, auto slot) {
         constexpr int d = decltype(slot)::value;
         constexpr int p = d & 1;
         constexpr int dn = (d + 1) % kBDist;
         const bool more = s + 1 < S;
-        constexpr int st = GATED ? d % kAStages : p;  // buffer read by this step
-        if constexpr (GATED)
-            dma_a(s + 3, (d + 3) % kAStages);
-        else if (more)
-            load_a(s + 1);
-        const uint8_t *ab = abase + st * kStage;
+        if (more) load_a(s + 1);
+        const uint8_t *ab = abase + p * kStageD;
         const Scales4 scn = scales4(bs[dn]);
         // Hand-ordered: row-tile operands are read two tiles ahead, and one
         // element pair of the next step's decode (4 VALU) follows every other
-        // MFMA, so that it issues in the matrix pipe's shadow.  Full
-        // scheduling fences keep this order; the empty asm after each decoded
-        // pair pins it there (otherwise it is sunk to its use in the next
-        // step).
+        // MFMA.  Full scheduling fences keep this order; the empty asm after
+        // each decoded pair pins it there (otherwise it is sunk to its use in
+        // the next step).
         bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab);
-        bf16x8_t an = *reinterpret_cast<const bf16x8_t *>(ab + 16 * kRow);
+        bf16x8_t an = *reinterpret_cast<const bf16x8_t *>(ab + 16 * kRowD);
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) {
-            const bf16x8_t an2 = *reinterpret_cast<const bf16x8_t *>(ab + (i + 2 < kMT ? i + 2 : kMT - 1) * 16 * kRow);
+        for (int i = 0; i < kMTD; ++i) {
+            const bf16x8_t an2 = *reinterpret_cast<const bf16x8_t *>(ab + (i + 2 < kMTD ? i + 2 : kMTD - 1) * 16 * kRowD);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -440,116 +606,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             an = an2;
         }
         load_b(s + 1 + kBDist, bw[dn], bs[dn]);
-        if constexpr (GATED) {
-            // Step s + 1's direct loads must have landed before the barrier.
-            // Loads issued after them (2 direct loads per step, 5 per
-            // refill; the prologue issued steps 0-2 after its refill):
-            //   s = 0:  step 2, then step 3 + refill            = 2 + 2 + 5
-            //   s = 1:  steps 3, 4 and two refills              = 2 * (2 + 5)
-            //   s >= 2: the refill after them, then two steps   = 5 + 2 * (2 + 5)
-            if (s == 0)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-            else if (s == 1)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(19));
-            block_barrier();
-        } else {
-            if (more) store_a(p ^ 1);
-            __syncthreads();
-        }
+        if (more) store_a(p ^ 1);
+        __syncthreads();
     };
-
-    // The step loop is unrolled by the ring depth so that ring slots, B
-    // operand parity and activation buffer are compile-time indices.
-    static_assert(kBDist == 2 || kBDist == 4, "ring depth");
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     int s0 = 0;
     for (; s0 + kBDist <= S; s0 += kBDist) {
         step(s0 + 0, I0{});
         step(s0 + 1, I1{});
-        if constexpr (kBDist == 4) {
-            step(s0 + 2, I2{});
-            step(s0 + 3, I3{});
-        }
+        step(s0 + 2, I2{});
+        step(s0 + 3, I3{});
     }
     if (s0 + 0 < S) step(s0 + 0, I0{});
-    if constexpr (kBDist == 4) {
-        if (s0 + 1 < S) step(s0 + 1, I1{});
-        if (s0 + 2 < S) step(s0 + 2, I2{});
-    }
-
-    if constexpr (GATED) {
-        // The last steps issued direct loads past the end (clamped repeats
-        // that keep the wait counts uniform); drain them before the epilogue
-        // reuses the buffers.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        block_barrier();
-    }
+    if (s0 + 1 < S) step(s0 + 1, I1{});
+    if (s0 + 2 < S) step(s0 + 2, I2{});
 
     // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j] ----
-    float *out = a.out;
-    if constexpr (!GATED) {
-        if (!wact) return;
-        const float s2 = a.s2a[e];
+    if (!wact) return;
+    const float s2 = a.s2a[e];
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) {
-            if (i < mt_used) {
+    for (int i = 0; i < kMTD; ++i) {
+        if (i < mt_used) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * i + 4 * q + v;
-                    if (row < mrows) {
-                        const float4 o = make_float4(acc[i][0][v] * s2, acc[i][1][v] * s2, acc[i][2][v] * s2,
-                                                     acc[i][3][v] * s2);
-                        *reinterpret_cast<float4 *>(out + (row0 + row) * N + n_w + 4 * c) = o;
-                    }
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * i + 4 * q + v;
+                if (row < mrows) {
+                    const float4 o = make_float4(acc[i][0][v] * s2, acc[i][1][v] * s2, acc[i][2][v] * s2,
+                                                 acc[i][3][v] * s2);
+                    *reinterpret_cast<float4 *>(a.out + (row0 + row) * N + n_w + 4 * c) = o;
                 }
-            }
-        }
-    } else {
-        // Up waves hand u = s2u * acc to the gate waves through LDS, kExRows rows per round.
-        const float s2g = a.s2a[e], s2u = a.s2b[e];
-        float *ex = reinterpret_cast<float *>(lds);
-        const int exc = 64 * (wave & 1) + 4 * c;  // column within the block's 128
-#pragma unroll
-        for (int i0 = 0; i0 < kMT; i0 += kExRows / 16) {
-            if (i0 < mt_used) {
-                if (up_wave) {
-#pragma unroll
-                    for (int i = i0; i < i0 + kExRows / 16 && i < kMT; ++i) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int rl = 16 * (i - i0) + 4 * q + v;
-                            *reinterpret_cast<float4 *>(ex + rl * 128 + exc) =
-                                make_float4(acc[i][0][v] * s2u, acc[i][1][v] * s2u, acc[i][2][v] * s2u,
-                                            acc[i][3][v] * s2u);
-                        }
-                    }
-                }
-                __syncthreads();
-                if (!up_wave && wact) {
-#pragma unroll
-                    for (int i = i0; i < i0 + kExRows / 16 && i < kMT; ++i) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int rl = 16 * (i - i0) + 4 * q + v;
-                            const int row = 16 * i + 4 * q + v;
-                            if (row < mrows) {
-                                const float4 u = *reinterpret_cast<const float4 *>(ex + rl * 128 + exc);
-                                float4 o;
-                                o.x = moe::silu_f32(acc[i][0][v] * s2g) * u.x;
-                                o.y = moe::silu_f32(acc[i][1][v] * s2g) * u.y;
-                                o.z = moe::silu_f32(acc[i][2][v] * s2g) * u.z;
-                                o.w = moe::silu_f32(acc[i][3][v] * s2g) * u.w;
-                                *reinterpret_cast<float4 *>(out + (row0 + row) * N + n_w + 4 * c) = o;
-                            }
-                        }
-                    }
-                }
-                __syncthreads();
             }
         }
     }
@@ -579,15 +663,15 @@ int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_to
     const int cols = gated ? 128 : 256;
     a.n_ct = (N + cols - 1) / cols;
     // Row tiles: sum over experts of ceil(rows / R) <= ceil(P / R) + min(E, P).
-    const int rows = gated ? Tile<true>::kMaxRows : Tile<false>::kMaxRows;
+    const int rows = gated ? kRowsG : kRowsD;
     const int cap = E < P ? E : P;
     const long long mt_bound = (P + rows - 1) / rows + cap;
     const long long units = mt_bound * a.n_ct;
     const long long grid = ((units + 7) / 8) * 8;
     if (grid > 0x7fffffffLL) return MOE_NVFP4_ELIMIT;
     if (gated)
-        hipLaunchKernelGGL(k_gemm_kmajor<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_gemm_gate_up, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(k_gemm_kmajor<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_gemm_down, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return moe_host::launch_status();
 }
