@@ -11,6 +11,7 @@ from .moe_oracle import (  # noqa: F401
     expert_weights,
     gate_up_silu_rows,
     moe_layer,
+    route_topk,
     silu,
     sort_routes,
     transpose_u8,

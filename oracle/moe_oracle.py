@@ -122,6 +122,38 @@ def transpose_u8(src: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Router (ahead of the path: softmax over the expert logits, top k kept,
+# weights renormalised over them).  The pages show only the router's logit
+# GEMM (prefill_weights.rs page, doc of dense_gemm_prefill: the gate GEMM);
+# the selection and weights follow the routing the workloads are defined by.
+# --------------------------------------------------------------------------
+def route_topk(logits: np.ndarray, k: int):
+    """Top-k routing of each row of f32 logits [T, E].
+
+    ids: the k largest logits of the row in descending order, equal logits by
+    lower expert id, NaN below every number (-0.0 equals +0.0).
+    weights (float64): softmax renormalised over the selected experts,
+    p_j / sum_i p_i with p = softmax(row); the full denominator cancels, so
+    w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the selected i.
+    """
+    assert logits.dtype == np.float32 and logits.ndim == 2
+    T, E = logits.shape
+    assert 1 <= k <= E
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        row = logits[t].astype(np.float64)
+        key = np.where(np.isnan(row), -np.inf, row)          # NaN ranks lowest...
+        nan_last = np.isnan(row).astype(np.int64)             # ...even below -inf
+        order = np.lexsort((np.arange(E), nan_last, -key))[:k]
+        ids[t] = order
+        sel = row[order]
+        z = np.exp(sel - sel[0])
+        w[t] = z / z.sum()
+    return ids, w
+
+
+# --------------------------------------------------------------------------
 # Routing sort
 # --------------------------------------------------------------------------
 def sort_routes(topk_ids: np.ndarray, E: int) -> dict:

@@ -14,6 +14,7 @@ from .moe_inputs import (  # noqa: F401
     config,
     expert_bytes,
     gen_expert,
+    gen_logits,
     gen_routing,
     gen_x,
     proj_dims,

@@ -101,6 +101,19 @@ def gen_x(cfg_id: int, shape: MoeShape | None = None, batch: int = 0) -> np.ndar
     return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def gen_logits(cfg_id: int, shape: MoeShape | None = None, batch: int = 0) -> np.ndarray:
+    """Router logits float32 [T, E]: the draw behind ``gen_routing`` (with
+    the Zipf bias where the workload has one), rounded to f32."""
+    shape = shape or config(cfg_id)
+    logits = _rng(cfg_id, 2, batch).standard_normal((shape.T, shape.E))
+    if shape.routing == "zipf":
+        rank = 1 + _rng(cfg_id, 3).permutation(shape.E)
+        logits = logits - shape.zipf_s * np.log(rank.astype(np.float64))[None, :]
+    elif shape.routing != "uniform":
+        raise ValueError(shape.routing)
+    return logits.astype(np.float32)
+
+
 def gen_routing(cfg_id: int, shape: MoeShape | None = None, batch: int = 0):
     """Router output: (topk_ids int32 [T, k], topk_weights float32 [T, k]);
     ``batch`` selects an independent draw (the Zipf rank order is shared)."""

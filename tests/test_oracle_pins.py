@@ -153,6 +153,59 @@ def _brute_sort(ids, E):
     return offs, stok, pos, act + [-1] * (E - len(act)), len(act), int(len(valid) != P)
 
 
+# ---------------------------------------------------------------- router (next step F1)
+def _router_rows(seed, T, E):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    # plant exact ties, signed zeros and NaN
+    lg[0, 1] = lg[0, 3]
+    lg[0, E - 1] = lg[0, 3]
+    lg[1, :] = 0.0
+    lg[1, 2] = -0.0
+    lg[2, 0] = np.nan
+    lg[2, 5] = np.nan
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(6, 8, 3, 0), (5, 16, 16, 1), (4, 64, 8, 2), (3, 7, 1, 3)])
+def test_router_bruteforce(T, E, k, seed):
+    """Scalar brute force: rank by (NaN last, larger logit, lower id); weights
+    exp(l - l_max) normalised with math.exp over the selected experts."""
+    lg = _router_rows(seed, T, E)
+    ids, w = oracle.route_topk(lg, k)
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        order = sorted(range(E), key=lambda e: (math.isnan(row[e]), -row[e] if not math.isnan(row[e]) else 0.0, e))
+        assert ids[t].tolist() == order[:k]
+        sel = [row[e] for e in order[:k]]
+        ex = [math.exp(v - sel[0]) for v in sel]
+        tot = math.fsum(ex)
+        for j in range(k):
+            if math.isnan(ex[j]) or math.isnan(tot):
+                assert math.isnan(w[t, j])
+            else:
+                assert abs(w[t, j] - ex[j] / tot) <= 1e-15
+    # ties resolve to the lower id; -0.0 ties +0.0
+    if k >= 2 and E > 3:
+        assert ids[1, :k].tolist() == list(range(k))
+
+
+def test_router_equals_renormalised_full_softmax():
+    """The weights equal softmax over all experts (scipy) restricted to the
+    selected ones and renormalised: the full denominator cancels."""
+    from scipy.special import softmax
+
+    lg = synth.gen_logits(3)
+    ids, w = oracle.route_topk(lg, 6)
+    p = softmax(lg.astype(np.float64), axis=1)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-12, atol=0)
+    assert np.all(np.diff(np.take_along_axis(lg, ids.astype(np.int64), axis=1), axis=1) <= 0)
+    # scaling by 2 (exact in f32) keeps the selection
+    ids2, _ = oracle.route_topk(lg * np.float32(2.0), 6)
+    assert np.array_equal(ids, ids2)
+
+
 @pytest.mark.parametrize("T,k,E,seed", [(4, 2, 4, 0), (1, 8, 128, 1), (32, 6, 128, 2), (7, 3, 5, 3), (50, 4, 9, 4)])
 def test_sort_bruteforce(T, k, E, seed):
     rng = np.random.default_rng(seed)
