@@ -197,6 +197,28 @@ int moe_nvfp4_blend(const float *y, const float *topk_weights, const int32_t *pa
  */
 int transpose_u8(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, void *stream);
 
+/*
+ * moe_nvfp4_route — router ahead of the path: softmax over each token's
+ * expert logits, the k largest kept, weights renormalised over them.  The
+ * pages show only the router's logit GEMM (prefill_weights.rs, doc of
+ * dense_gemm_prefill: the gate GEMM); the outputs are the topk_ids and
+ * topk_weights that moe_nvfp4_sort and moe_nvfp4_blend take.
+ *
+ *   logits        in  f32 [T, E]
+ *   topk_ids      out int32 [T, k]  the k largest logits of row t in
+ *                                   descending order; equal logits by lower
+ *                                   expert id; -0.0 equals +0.0; NaN below
+ *                                   every number.
+ *   topk_weights  out f32 [T, k]    exp(l_j - l_max) / sum_i exp(l_i - l_max)
+ *                                   over the k selected (equal to the softmax
+ *                                   over all E renormalised over them); NaN
+ *                                   where a selected logit is NaN or infinite.
+ * Errors: ENULL; ESHAPE if T < 1, E < 1, k < 1 or k > E; ELIMIT if
+ * E > MOE_NVFP4_MAX_EXPERTS, k > 64 or T * k > MOE_NVFP4_MAX_PAIRS.
+ */
+int moe_nvfp4_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                    float *topk_weights, void *stream);
+
 /* ABI version of the loaded library (MOE_NVFP4_ABI_VERSION). */
 int moe_nvfp4_abi_version(void);
 

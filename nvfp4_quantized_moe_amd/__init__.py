@@ -1,7 +1,7 @@
 """Grouped NVFP4 MoE expert projection for MI355X (gfx950).
 
-A thin ctypes binding over the C ABI in ``include/moe_nvfp4.h``: the five
-entry points keep their C names and take torch tensors only for device
+A thin ctypes binding over the C ABI in ``include/moe_nvfp4.h``: the entry
+points keep their C names and take torch tensors only for device
 memory and streams; every step of the path runs in the HIP kernels of
 ``libmoe_nvfp4.so``.  There is no CPU fallback: importing works without the
 library, but the first call raises if it is missing.
@@ -37,6 +37,7 @@ __all__ = [
     "moe_nvfp4_blend",
     "transpose_u8",
     "transpose_for_gemm",
+    "moe_nvfp4_route",
 ]
 
 ROW_MAJOR = 0
@@ -85,8 +86,9 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_down.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _P, _P, _P, _P, _P]
         L.moe_nvfp4_blend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
         L.transpose_u8.argtypes = [_P, _P, _I, _I, _P]
+        L.moe_nvfp4_route.argtypes = [_P, _I, _I, _I, _P, _P, _P]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
-                   "transpose_u8", "moe_nvfp4_abi_version"):
+                   "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -211,6 +213,16 @@ def transpose_u8(src, dst, rows, cols, stream=None) -> None:
     rc = lib().transpose_u8(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst"), rows, cols,
                             _stream(stream))
     _check("transpose_u8", rc)
+
+
+def moe_nvfp4_route(logits, k, topk_ids, topk_weights, stream=None) -> None:
+    """Router ahead of the path: top-k experts and renormalised softmax
+    weights of each row of f32 logits [T, E] (see the C header)."""
+    T, E = logits.shape
+    rc = lib().moe_nvfp4_route(_dev(logits, torch.float32, "logits"), T, E, k,
+                               _dev(topk_ids, torch.int32, "topk_ids"),
+                               _dev(topk_weights, torch.float32, "topk_weights"), _stream(stream))
+    _check("moe_nvfp4_route", rc)
 
 
 def transpose_for_gemm(packed: torch.Tensor, scale: torch.Tensor, n: int, k: int, group_size: int = 16):

@@ -82,3 +82,15 @@ def test_python_binding_checks_tensor_arguments():
         moe.transpose_u8(torch.zeros(4, dtype=torch.uint8), torch.zeros(4, dtype=torch.uint8), 2, 3)
     with pytest.raises((TypeError, ValueError)):
         moe.transpose_u8(torch.zeros(6, dtype=torch.uint8), torch.zeros(6, dtype=torch.uint8), 2, 3)
+
+
+def test_route_rejects():
+    L = moe.lib()
+    assert L.moe_nvfp4_route(None, 4, 8, 2, D, D, None) == ENULL
+    assert L.moe_nvfp4_route(D, 4, 8, 2, None, D, None) == ENULL
+    assert L.moe_nvfp4_route(D, 0, 8, 2, D, D, None) == ESHAPE
+    assert L.moe_nvfp4_route(D, 4, 8, 9, D, D, None) == ESHAPE    # k > E
+    assert L.moe_nvfp4_route(D, 4, 8, 0, D, D, None) == ESHAPE
+    assert L.moe_nvfp4_route(D, 4, 2000, 2, D, D, None) == ELIMIT  # E > MOE_NVFP4_MAX_EXPERTS
+    assert L.moe_nvfp4_route(D, 4, 128, 65, D, D, None) == ELIMIT  # k > 64
+    assert L.moe_nvfp4_route(D, 1 << 20, 8, 8, D, D, None) == ELIMIT  # T * k > MOE_NVFP4_MAX_PAIRS

@@ -302,3 +302,65 @@ def test_kmajor_few_experts_many_rows():
     say("K-major, few experts with many rows")
     shape = synth.MoeShape("tall", 700, 512, 640, 4, 2, "uniform", True)
     _full_check(Case(18, shape), "tall kmajor")
+
+
+# ---------------------------------------------------------------- router (next step F1)
+def _route_gpu(logits, k):
+    T, E = logits.shape
+    d = torch.from_numpy(logits).cuda()
+    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, k), -7.0, dtype=torch.float32, device="cuda")
+    moe.moe_nvfp4_route(d, k, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_route(logits, k, tag):
+    ids, w = _route_gpu(logits, k)
+    rids, rw = oracle.route_topk(logits, k)
+    assert np.array_equal(ids, rids), tag          # integer decisions from the same f32 comparisons
+    np.testing.assert_allclose(w.astype(np.float64), rw, rtol=1e-5, atol=1e-7, equal_nan=True, err_msg=tag)
+    say(tag, "max |dw|", float(np.nanmax(np.abs(w - rw))) if w.size else 0.0)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_router_configs(cfg):
+    say("router cfg", cfg)
+    s = synth.config(cfg)
+    _check_route(synth.gen_logits(cfg), s.k, f"router cfg{cfg}")
+
+
+@pytest.mark.parametrize("T,E,k,mode", [(1, 1, 1, "rand"), (9, 7, 7, "rand"), (5, 1024, 64, "rand"),
+                                         (33, 37, 5, "ties"), (6, 16, 4, "nan"), (200, 256, 8, "coarse")])
+def test_router_edge_cases(T, E, k, mode):
+    say("router edge", T, E, k, mode)
+    rng = np.random.default_rng(T * 13 + E * 7 + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if mode == "ties":
+        lg[:, ::3] = lg[:, :1]                     # many exact ties per row
+        lg[0, :] = 0.0
+        lg[0, 1::2] = -0.0
+    elif mode == "nan":
+        lg[0, 2] = np.nan
+        lg[1, :] = np.nan                           # all NaN: ids 0..k-1, weights NaN
+        lg[2, :3] = np.nan
+    elif mode == "coarse":
+        lg = np.round(lg * 4).astype(np.float32)    # few distinct values: ties everywhere
+    _check_route(lg, k, f"router {T},{E},{k},{mode}")
+
+
+def test_router_feeds_the_layer():
+    """Device router -> sort -> gate+up -> down -> blend equals the oracle
+    layer on the oracle's routing of the same logits (tiny workload)."""
+    say("router feeds the layer")
+    case = Case(1)
+    s = case.shape
+    logits = synth.gen_logits(1)
+    ids_d = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    moe.moe_nvfp4_route(torch.from_numpy(logits).cuda(), s.k, ids_d, w_d)
+    out = case.layer.forward(case.x, ids_d, w_d)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_topk(logits, s.k)
+    ref = oracle.moe_layer(case.x_bits, rids, rw.astype(np.float32), case.weight_fn(), s.E, s.H, s.I)
+    parity.assert_parity(_h2f(out), ref["out"], "routed layer")
