@@ -38,6 +38,7 @@ __all__ = [
     "transpose_u8",
     "transpose_for_gemm",
     "moe_nvfp4_route",
+    "with_shared_expert",
 ]
 
 ROW_MAJOR = 0
@@ -223,6 +224,27 @@ def moe_nvfp4_route(logits, k, topk_ids, topk_weights, stream=None) -> None:
                                _dev(topk_ids, torch.int32, "topk_ids"),
                                _dev(topk_weights, torch.float32, "topk_weights"), _stream(stream))
     _check("moe_nvfp4_route", rc)
+
+
+def with_shared_expert(topk_ids: torch.Tensor, topk_weights: torch.Tensor, shared_id: int):
+    """Routing that also sends every token to a shared expert with weight 1.
+
+    The pages run the shared expert in the same gate+up and down launches as
+    the routed ones, as extra block rows over all tokens, and add its output
+    in the blend (nvfp4_moe_grouped.rs, doc of
+    moe_expert_gate_up_act_nvfp4_grouped: the first block rows are the
+    shared expert, written to their own rows).  Here the shared expert is one
+    more slot of the expert tables (usually index E of E + 1) and this
+    appends it as a (k+1)-th route of every token: the sort gives it all T
+    rows, the same launches compute it with the routed experts, and the blend
+    adds it last with weight 1.  Returns new int32 [T, k+1] and f32 [T, k+1]
+    device tensors; call the layer with E + 1 experts and k + 1.
+    """
+    T = topk_ids.shape[0]
+    dev = topk_ids.device
+    ids = torch.cat([topk_ids, torch.full((T, 1), int(shared_id), dtype=torch.int32, device=dev)], dim=1)
+    w = torch.cat([topk_weights, torch.ones((T, 1), dtype=torch.float32, device=dev)], dim=1)
+    return ids.contiguous(), w.contiguous()
 
 
 def transpose_for_gemm(packed: torch.Tensor, scale: torch.Tensor, n: int, k: int, group_size: int = 16):

@@ -364,3 +364,20 @@ def test_router_feeds_the_layer():
     rids, rw = oracle.route_topk(logits, s.k)
     ref = oracle.moe_layer(case.x_bits, rids, rw.astype(np.float32), case.weight_fn(), s.E, s.H, s.I)
     parity.assert_parity(_h2f(out), ref["out"], "routed layer")
+
+
+# ---------------------------------------------------------------- shared expert (next step F2)
+@pytest.mark.parametrize("kmajor", [False, True])
+def test_shared_expert_in_the_same_launches(kmajor):
+    """Every token also routes to a shared expert (table slot E, weight 1):
+    the four launches compute it with the routed experts; the output matches
+    the oracle layer on the same extended routing."""
+    say("shared expert", "kmajor" if kmajor else "row-major")
+    base = synth.config(3)
+    ids, w = synth.gen_routing(3, base)
+    ids_d, w_d = moe.with_shared_expert(torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), base.E)
+    aug_ids, aug_w = ids_d.cpu().numpy(), w_d.cpu().numpy()
+    assert np.array_equal(aug_ids[:, :-1], ids) and np.all(aug_ids[:, -1] == base.E)
+    assert np.array_equal(aug_w[:, :-1], w) and np.all(aug_w[:, -1] == 1.0)
+    shape = synth.MoeShape("shared3", base.T, base.H, base.I, base.E + 1, base.k + 1, "zipf", kmajor)
+    _full_check(Case(3, shape, ids=aug_ids, weights=aug_w), f"shared {kmajor}")

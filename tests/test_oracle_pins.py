@@ -206,6 +206,32 @@ def test_router_equals_renormalised_full_softmax():
     assert np.array_equal(ids, ids2)
 
 
+# ---------------------------------------------------------------- shared expert (next step F2)
+def test_shared_expert_as_extra_route_equals_dense_swiglu_added():
+    """A shared expert routed to every token with weight 1 (one more table
+    slot, one more route per token) adds exactly the dense SwiGLU of its
+    weights to the routed layer: oracle layer with the extra route versus
+    the routed oracle layer plus a torch fp64 SwiGLU."""
+    s = synth.config(1)
+    Es = s.E + 1
+    shape = synth.MoeShape("shared", s.T, s.H, s.I, Es, s.k + 1, "uniform", False)
+    x_bits = synth.gen_x(1, s)
+    ids, w = synth.gen_routing(1, s)
+    aug_ids = np.concatenate([ids, np.full((s.T, 1), s.E, np.int32)], axis=1)
+    aug_w = np.concatenate([w, np.ones((s.T, 1), np.float32)], axis=1)
+
+    def wf(e, proj):
+        pk, sc = synth.gen_expert(1, e, proj, shape)
+        return pk, sc, synth.SCALE2_F32
+
+    with_shared = oracle.moe_layer(x_bits, aug_ids, aug_w, wf, Es, s.H, s.I)["out"]
+    routed = oracle.moe_layer(x_bits, ids, w, wf, s.E, s.H, s.I)["out"]
+    Wg, Wu, Wd = (torch.from_numpy(m) for m in oracle.expert_weights(wf, s.E, s.H, s.I, False))
+    x = torch.from_numpy(oracle.bf16_bits_to_f64(x_bits))
+    dense = (F.silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    np.testing.assert_allclose(with_shared, routed + dense.numpy(), rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("T,k,E,seed", [(4, 2, 4, 0), (1, 8, 128, 1), (32, 6, 128, 2), (7, 3, 5, 3), (50, 4, 9, 4)])
 def test_sort_bruteforce(T, k, E, seed):
     rng = np.random.default_rng(seed)
