@@ -21,6 +21,8 @@ instead).  Reported on one JSON line:
               matrix-core peak); traffic = HBM bytes per launch from the
               committed counter summary in profiles/ while the kernel sources
               are unchanged since it was taken, else null
+  router      launch time of moe_nvfp4_route on the workload's logits (the
+              router ahead of the path; not part of the step)
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
               same workload, in the same unit
 """
@@ -307,7 +309,7 @@ def main():
     gu_bytes = float(gate_up_bytes(shape, idss[0]))
     traffic = measured_traffic(shape.name)
     if shape.kmajor:
-        # Many-token path: a dense fp16 contraction on the matrix cores.
+        # Many-token path: a dense bf16 contraction on the matrix cores.
         flops = 4.0 * shape.P * shape.I * shape.H  # gate and up, 2 flops per MAC
         roof = {"bound": "mfma", "achieved": round(flops / (gu_ms / 1e3) / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
@@ -319,6 +321,22 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof.update({"traffic": traffic, "kernel": "moe_nvfp4_gate_up_silu", "launch_us": round(gu_ms * 1e3, 3),
                  "algorithmic_bytes_per_launch": round(gu_bytes)})
+
+    # ---- the router ahead of the path (softmax, top-k, renormalise), timed
+    # on its own over the workload's logits; it is not part of the step.
+    logits_d = torch.from_numpy(synth.gen_logits(cfg_id, shape)).to(dev)
+    r_ids = torch.empty((shape.T, shape.k), dtype=torch.int32, device=dev)
+    r_w = torch.empty((shape.T, shape.k), dtype=torch.float32, device=dev)
+    Kq = 100
+    with torch.cuda.stream(stream):
+        for rep in range(2):
+            e0.record(stream)
+            for i in range(Kq):
+                moe.moe_nvfp4_route(logits_d, shape.k, r_ids, r_w, stream)
+            e1.record(stream)
+    torch.cuda.synchronize()
+    router = {"kernel": "moe_nvfp4_route", "launch_us": round(e0.elapsed_time(e1) / Kq * 1e3, 3),
+              "in_step": False}
 
 
     line = {
@@ -345,6 +363,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "active_weight_bytes_per_step": round(bytes_timed / K),
         "roofline": roof,
+        "router": router,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
