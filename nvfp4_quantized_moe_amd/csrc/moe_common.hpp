@@ -102,6 +102,32 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Wave-wide extrema of a 32-bit unsigned value: DPP within each 16-lane row
+// (every lane of a row reads a valid source in these patterns), then the
+// four row results through readlane, so the result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<kDppXor1>(v));
+    v = min(v, dpp_u32<kDppXor2>(v));
+    v = min(v, dpp_u32<kDppHalfMirror>(v));
+    v = min(v, dpp_u32<kDppMirror>(v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
     return z / (1.0f + __expf(-z));
 }

@@ -161,26 +161,12 @@ __device__ __forceinline__ void put_f16x8(uint16_t *dst, const f32x4_t &a, const
 // values: the first and the last lane's rows get one atomic each after a wave
 // reduction; lanes of any row strictly between (short rows only) post their
 // own.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-// Wave maximum: DPP within each 16-lane row, then the four row results.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<moe::kDppXor1>(v));
-    v = max(v, dpp_u32<moe::kDppXor2>(v));
-    v = max(v, dpp_u32<moe::kDppHalfMirror>(v));
-    v = max(v, dpp_u32<moe::kDppMirror>(v));
-    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
-}
 __device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v) {
     const int lane = threadIdx.x & 63;
     const int m_lo = __builtin_amdgcn_readfirstlane(m);
     const int m_hi = __builtin_amdgcn_readlane(m, 63);
-    const uint32_t lo = wave_max_u32(m == m_lo ? v : 0u);
-    const uint32_t hi = wave_max_u32(m == m_hi ? v : 0u);
+    const uint32_t lo = moe::wave_max_u32(m == m_lo ? v : 0u);
+    const uint32_t hi = moe::wave_max_u32(m == m_hi ? v : 0u);
     if (lane == 0) atomicMax(rmax + m_lo, lo);
     if (lane == 63 && m_hi != m_lo) atomicMax(rmax + m_hi, hi);
     if (m != m_lo && m != m_hi) atomicMax(rmax + m, v);

@@ -6,7 +6,8 @@
 //
 // One wavefront per token: each lane holds up to 16 of the E logits (expert
 // lane + 64 i) as order keys; k rounds of a wave-wide argmax (larger key
-// first, then lower expert id) pick the experts in descending order.  The
+// first, then lower expert id; a DPP maximum of the keys, then a DPP minimum
+// of the ids holding it) pick the experts in descending order.  The
 // softmax denominator over all E cancels in the renormalisation, so the
 // weights are exp(l_j - l_max) over the k selected, summed across the wave.
 #include "moe_common.hpp"
@@ -25,6 +26,7 @@ __device__ __forceinline__ uint32_t rank_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int PER>  // logits held per lane: E <= 64 * PER
 __global__ __launch_bounds__(kThreads) void k_route(const float *__restrict__ logits, int T, int E, int k,
                                                     int32_t *__restrict__ ids, float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
@@ -32,11 +34,11 @@ __global__ __launch_bounds__(kThreads) void k_route(const float *__restrict__ lo
     if (t >= T) return;  // the whole wavefront
     const float *row = logits + (size_t)t * E;
 
-    uint32_t key[kPerLane];
-    float val[kPerLane];
+    uint32_t key[PER];
+    float val[PER];
     uint32_t taken = 0;  // bit i: candidate lane + 64 i selected already, or beyond E
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < PER; ++i) {
         const int e = lane + moe::kWave * i;
         if (e < E) {
             val[i] = row[e];
@@ -50,41 +52,30 @@ __global__ __launch_bounds__(kThreads) void k_route(const float *__restrict__ lo
 
     float mine = 0.f;  // logit selected in round `lane`
     for (int r = 0; r < k; ++r) {
-        // This lane's best remaining candidate; "none" is (0, INT_MAX), below
-        // a NaN candidate (0, e).  Candidates are visited in ascending id, so
-        // a strict comparison keeps the lower id on equal keys.
-        uint32_t bk = 0u;
-        int be = 0x7fffffff;
+        // This lane's best remaining candidate (largest key, lowest id on
+        // equal keys: candidates are visited in ascending id); "none" has id
+        // 0xffffffff, so it loses to any candidate, NaN ones included.
+        uint32_t bk = 0u, be = 0xffffffffu;
         float bv = 0.f;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = lane + moe::kWave * i;
-            if (!((taken >> i) & 1u) && (key[i] > bk || be == 0x7fffffff)) {
+        for (int i = 0; i < PER; ++i) {
+            if (!((taken >> i) & 1u) && (key[i] > bk || be == 0xffffffffu)) {
                 bk = key[i];
-                be = e;
+                be = (uint32_t)(lane + moe::kWave * i);
                 bv = val[i];
             }
         }
-        // Wave-wide argmax over (key descending, id ascending): a total order,
-        // so every lane ends with the same winner.
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            const uint32_t ok = __shfl_xor(bk, d, 64);
-            const int oe = __shfl_xor(be, d, 64);
-            const float ov = __shfl_xor(bv, d, 64);
-            if (ok > bk || (ok == bk && oe < be)) {
-                bk = ok;
-                be = oe;
-                bv = ov;
-            }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == r) mine = bv;
-        if (lane == 0) ids[(size_t)t * k + r] = be;
+        // Wave-wide winner: the largest key, then the lowest id holding it.
+        const uint32_t mk = moe::wave_max_u32(bk);
+        const uint32_t me = moe::wave_min_u32(bk == mk ? be : 0xffffffffu);
+        const float mv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), me & 63));
+        if ((int)(me & 63) == lane) taken |= 1u << (me >> 6);
+        if (lane == r) mine = mv;
+        if (lane == 0) ids[(size_t)t * k + r] = (int32_t)me;
     }
 
     // Renormalised softmax over the k selected (round 0 holds the largest).
-    const float lmax = __shfl(mine, 0, 64);
+    const float lmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mine)));
     const float ex = lane < k ? expf(mine - lmax) : 0.f;
     float sum = ex;
 #pragma unroll
@@ -101,7 +92,17 @@ extern "C" int moe_nvfp4_route(const float *logits, int32_t T, int32_t E, int32_
     if (E > MOE_NVFP4_MAX_EXPERTS || k > kMaxK || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
     const int per_block = kThreads / moe::kWave;
     const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
-    hipLaunchKernelGGL(k_route, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, logits, T, E, k, topk_ids,
-                       topk_weights);
+    const hipStream_t st = (hipStream_t)stream;
+    if (E <= 64)
+        hipLaunchKernelGGL(k_route<1>, dim3(grid), dim3(kThreads), 0, st, logits, T, E, k, topk_ids, topk_weights);
+    else if (E <= 128)
+        hipLaunchKernelGGL(k_route<2>, dim3(grid), dim3(kThreads), 0, st, logits, T, E, k, topk_ids, topk_weights);
+    else if (E <= 256)
+        hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kThreads), 0, st, logits, T, E, k, topk_ids, topk_weights);
+    else if (E <= 512)
+        hipLaunchKernelGGL(k_route<8>, dim3(grid), dim3(kThreads), 0, st, logits, T, E, k, topk_ids, topk_weights);
+    else
+        hipLaunchKernelGGL(k_route<kPerLane>, dim3(grid), dim3(kThreads), 0, st, logits, T, E, k, topk_ids,
+                           topk_weights);
     return moe_host::launch_status();
 }
