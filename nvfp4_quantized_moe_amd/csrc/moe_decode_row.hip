@@ -583,13 +583,23 @@ template <bool GATED>
 __device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, uint8_t *lds) {
     const int e = a.active[slot];  // -1 past the active count
     if (e < 0) return;
-    const int lo = a.offsets[e], rows = a.offsets[e + 1] - lo;
+    // Every table entry of expert e is read at once (e < E, so each read is
+    // in bounds): one round of dependent loads after the active list, not
+    // one per table.
+    const int lo = a.offsets[e], hi = a.offsets[e + 1];
+    const uint8_t *pA = a.pa[e];
+    const uint8_t *pB = GATED ? a.pb[e] : pA;
+    const uint8_t *sA = a.sa[e];
+    const uint8_t *sB = GATED ? a.sb[e] : sA;
+    const float s2A = a.s2a[e];
+    const float s2B = GATED ? a.s2b[e] : s2A;
+    // Hold the reads here: otherwise they sink below the branches that follow.
+    asm volatile("" ::"s"(lo), "s"(hi), "s"(pA), "s"(pB), "s"(sA), "s"(sB), "s"(s2A), "s"(s2B));
+    const int rows = hi - lo;
     const int m0 = pass * a.pass_rows;
     if (m0 >= rows) return;
     const int pr = min(a.pass_rows, rows - m0);
     constexpr int ucols = GATED ? 16 : 32;
-    const uint8_t *pA = a.pa[e];
-    const uint8_t *pB = GATED ? a.pb[e] : pA;
     if (pA == nullptr || pB == nullptr) {  // absent expert: its rows are zero
         const int ncols = nu * ucols, n0 = u_first * ucols;
         for (int i = threadIdx.x; i < pr * ncols; i += kThreads) {
@@ -598,10 +608,6 @@ __device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, in
         }
         return;
     }
-    const uint8_t *sA = a.sa[e];
-    const uint8_t *sB = GATED ? a.sb[e] : sA;
-    const float s2A = a.s2a[e];
-    const float s2B = GATED ? a.s2b[e] : s2A;
     run_pass<GATED, kDepth>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
 }
 
