@@ -25,6 +25,11 @@ mixture-of-experts over NVFP4-dequantised weights, in float64, step by step:
      ``moe_expert_down_act_nvfp4_grouped``).
   5. Weighted top-k blend (same page, module doc: the weighted-sum blend).
 
+MXFP4 experts (transpose.rs page, doc of ``transpose_for_gemm``: experts in
+native MXFP4 use a scale group of 32; doc of ``transpose_for_gemm_gs``: the
+scale tensor is [N, K / group]): the same E2M1 codes with one E8M0 scale per
+32 values, W[n, k] = e2m1(nibble) * e8m0(scale[n, k // 32]) * scale_2.
+
 Readings where the pages are silent (each listed in the design notes):
   * E2M1 is the OCP FP4 format (1 sign, 2 exponent bits with bias 1,
     1 mantissa bit; code 0b?001 is the subnormal 0.5).
@@ -32,6 +37,8 @@ Readings where the pages are silent (each listed in the design notes):
     only at S.1111.111, largest finite 448 (prefill_weights.rs page, the
     shared-expert copies, gives 448 as the E4M3 saturation point).
   * The low nibble of a packed byte holds the even k.
+  * E8M0 (the MXFP4 scale) is the OCP MX scale format: the byte is a biased
+    exponent, value 2^(code - 127), code 255 is NaN; no sign, no mantissa.
   * The sort is stable by flat pair index t*k + j; active experts ascend.
   * Pairs whose expert id lies outside [0, E) belong to no expert: they
     raise the error flag, get position -1 and contribute zero.
@@ -76,8 +83,19 @@ def e4m3fn_value(code: int) -> float:
     return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
 
 
+def e8m0_value(code: int) -> float:
+    """Value of an 8-bit E8M0 scale code: 2^(code - 127); code 255 is NaN."""
+    if code == 255:
+        return math.nan
+    return math.ldexp(1.0, code - 127)
+
+
 E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 E4M3FN = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+E8M0 = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+
+# Scale format of each weight format: (values per scale, scale code table).
+FORMATS = {"nvfp4": (16, E4M3FN), "mxfp4": (32, E8M0)}
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -89,26 +107,29 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # NVFP4 dequantisation
 # --------------------------------------------------------------------------
-def dequant(packed: np.ndarray, scale: np.ndarray, scale2, n: int, k: int, kmajor: bool = False) -> np.ndarray:
-    """Dequantise one NVFP4 projection to float64 [n, k].
+def dequant(packed: np.ndarray, scale: np.ndarray, scale2, n: int, k: int, kmajor: bool = False,
+            fmt: str = "nvfp4") -> np.ndarray:
+    """Dequantise one projection to float64 [n, k].
 
-    Row-major: packed [n, k/2], scale [n, k/16].  K-major twin: packed
-    [k/2, n], scale [k/16, n].  Element (n, k) reads nibble (k & 1) of byte
-    (n, k >> 1) and scale byte (n, k >> 4).  Exact in float64 (at most
-    2 + 4 + 24 significant bits).
+    NVFP4 (group g = 16, E4M3 scales) or MXFP4 (g = 32, E8M0 scales).
+    Row-major: packed [n, k/2], scale [n, k/g].  K-major twin: packed
+    [k/2, n], scale [k/g, n].  Element (n, k) reads nibble (k & 1) of byte
+    (n, k >> 1) and scale byte (n, k // g).  Exact in float64 (NVFP4: at
+    most 2 + 4 + 24 significant bits; MXFP4: the scale is a power of two).
     """
+    g, table = FORMATS[fmt]
     if kmajor:
-        assert packed.shape == (k // 2, n) and scale.shape == (k // 16, n)
+        assert packed.shape == (k // 2, n) and scale.shape == (k // g, n)
         pb = packed.T
         sb = scale.T
     else:
-        assert packed.shape == (n, k // 2) and scale.shape == (n, k // 16)
+        assert packed.shape == (n, k // 2) and scale.shape == (n, k // g)
         pb = packed
         sb = scale
     kk = np.arange(k)
     byte = pb[:, kk >> 1].astype(np.uint8)
     code = (byte >> (4 * (kk & 1)).astype(np.uint8)) & 0xF
-    s = E4M3FN[sb[:, kk >> 4]]
+    s = table[sb[:, kk // g]]
     return E2M1[code] * s * float(np.float32(scale2))
 
 
@@ -228,17 +249,17 @@ def blend(y: np.ndarray, topk_weights: np.ndarray, pair_pos: np.ndarray) -> np.n
 WeightFn = Callable[[int, int], Optional[tuple]]
 
 
-def expert_weights(weights: WeightFn, e: int, H: int, I: int, kmajor: bool):
+def expert_weights(weights: WeightFn, e: int, H: int, I: int, kmajor: bool, fmt: str = "nvfp4"):
     """Dequantised (Wg [I,H], Wu [I,H], Wd [H,I]) of expert e, or None if it is NULL."""
     parts = [weights(e, p) for p in (0, 1, 2)]
     if any(p is None for p in parts):
         return None
     dims = ((I, H), (I, H), (H, I))
-    return tuple(dequant(pk, sc, s2, n, kk, kmajor) for (pk, sc, s2), (n, kk) in zip(parts, dims))
+    return tuple(dequant(pk, sc, s2, n, kk, kmajor, fmt) for (pk, sc, s2), (n, kk) in zip(parts, dims))
 
 
 def moe_layer(x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
-              weights: WeightFn, E: int, H: int, I: int, kmajor: bool = False) -> dict:
+              weights: WeightFn, E: int, H: int, I: int, kmajor: bool = False, fmt: str = "nvfp4") -> dict:
     """The whole path: sort, gate+up+SiLU, down, blend.  Returns the sort
     outputs plus float64 h [P, I], y [P, H] and out [T, H]."""
     T, k = topk_ids.shape
@@ -250,7 +271,7 @@ def moe_layer(x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray
     offs = srt["expert_offsets"]
     for e in srt["active_experts"][: srt["active_count"]]:
         lo, hi = int(offs[e]), int(offs[e + 1])
-        W = expert_weights(weights, int(e), H, I, kmajor)
+        W = expert_weights(weights, int(e), H, I, kmajor, fmt)
         if W is None:
             continue
         Wg, Wu, Wd = W

@@ -11,9 +11,11 @@ from .moe_inputs import (  # noqa: F401
     PROJ_GATE,
     PROJ_UP,
     SCALE2_F32,
+    SCALE2_MX_F32,
     config,
     expert_bytes,
     gen_expert,
+    gen_expert_mx,
     gen_logits,
     gen_routing,
     gen_x,

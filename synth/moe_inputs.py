@@ -9,6 +9,7 @@ projection can be regenerated on its own:
     tag 3  Zipf rank permutation        (a = b = 0)
     tag 4  packed E2M1 bytes            (a = expert, b = projection)
     tag 5  E4M3 block-scale codes       (a = expert, b = projection)
+    tag 6  E8M0 block-scale codes       (a = expert, b = projection; MXFP4)
 
 Projection ids: 0 = gate, 1 = up, 2 = down.  Gate and up are ``[N=I, K=H]``,
 down is ``[N=H, K=I]``; all are generated row-major (packed ``[N, K/2]``,
@@ -21,6 +22,11 @@ Value distributions (one per input, stated by the workload definitions):
   * block scales: a real ``u ~ U[2^-4, 2^2]`` encoded to the nearest E4M3
     (FN variant) code by torch's float8_e4m3fn cast, ties to even;
   * per-tensor scale_2 = float32(1 / (448 * 6)) for every projection;
+  * MXFP4 weights (the many-token shape with native-MXFP4 experts): the
+    same packed bytes; E8M0 scale codes uniform over the integers
+    112..118 (scales 2^-15 .. 2^-9, the magnitude range of the NVFP4
+    weights above: E4M3 scales in [2^-4, 2^2] times 1/2688 ~ 2^-11.4);
+    scale_2 = 1 (MXFP4 has no per-tensor scale);
   * x: standard normal float32, rounded to bf16 (nearest-even) by torch;
   * router: standard-normal logits (plus, for the skewed workload, a Zipf
     bias ``-s * ln(rank)`` over a seeded rank permutation of the experts),
@@ -38,6 +44,7 @@ import torch
 
 PROJ_GATE, PROJ_UP, PROJ_DOWN = 0, 1, 2
 SCALE2_F32 = np.float32(1.0 / (448.0 * 6.0))
+SCALE2_MX_F32 = np.float32(1.0)
 _SEED_ROOT = 2026
 
 
@@ -143,4 +150,13 @@ def gen_expert(cfg_id: int, e: int, proj: int, shape: MoeShape | None = None):
     packed = _rng(cfg_id, 4, e, proj).integers(0, 256, size=(n, k // 2), dtype=np.uint8)
     u = _rng(cfg_id, 5, e, proj).uniform(2.0 ** -4, 4.0, size=(n, k // 16)).astype(np.float32)
     scale = torch.from_numpy(u).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return packed, scale
+
+
+def gen_expert_mx(cfg_id: int, e: int, proj: int, shape: MoeShape | None = None):
+    """One row-major MXFP4 projection: (packed uint8 [N, K/2], E8M0 scale codes uint8 [N, K/32])."""
+    shape = shape or config(cfg_id)
+    n, k = proj_dims(shape, proj)
+    packed = _rng(cfg_id, 4, e, proj).integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scale = _rng(cfg_id, 6, e, proj).integers(112, 119, size=(n, k // 32), dtype=np.uint8)
     return packed, scale

@@ -119,6 +119,100 @@ def _golden_e2m1_arr():
     return [d[c] for c in range(16)]
 
 
+# ---------------------------------------------------------------- MXFP4: E8M0 scales, group 32
+def test_e8m0_matches_torch_float8_e8m0fnu_all_codes():
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    ours = oracle.E8M0
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(ours)) and set(np.nonzero(nan)[0]) == {0xFF}
+    assert np.array_equal(lib[~nan], ours[~nan])
+
+
+def test_e8m0_matches_ocp_mx_points():
+    rows = _golden("e8m0_ocp_mx_points.txt")
+    for code, v in rows:
+        got = oracle.E8M0[code]
+        assert (math.isnan(got) and math.isnan(v)) or got == v, (hex(code), got, v)
+    # every finite code is a power of two and consecutive codes double
+    fin = oracle.E8M0[:255]
+    assert np.all(fin[1:] == 2 * fin[:-1]) and fin[127] == 1.0
+
+
+def _scalar_dequant_mx(packed, scale, s2, n, k):
+    """Scalar MXFP4 decode written independently of the oracle tables:
+    E2M1 from the golden table, E8M0 through torch's float8_e8m0fnu."""
+    e2m1 = dict(_golden("e2m1_ocp_mx.txt"))
+    e8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().tolist()
+    byte = int(packed[n, k // 2])
+    nib = (byte & 0xF) if k % 2 == 0 else (byte >> 4)
+    return e2m1[nib] * e8[int(scale[n, k // 32])] * float(np.float32(s2))
+
+
+def test_mx_dequant_bruteforce_points_and_layouts():
+    rng = np.random.default_rng(11)
+    n, k = 20, 160
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scale = rng.integers(0, 255, (n, k // 32), dtype=np.uint8)
+    s2 = np.float32(1.0)
+    W = oracle.dequant(packed, scale, s2, n, k, fmt="mxfp4")
+    for i in range(n):
+        for j in range(k):
+            assert W[i, j] == _scalar_dequant_mx(packed, scale, s2, i, j)
+    Wt = oracle.dequant(oracle.transpose_u8(packed), oracle.transpose_u8(scale), s2, n, k, kmajor=True,
+                        fmt="mxfp4")
+    assert np.array_equal(W, Wt)
+
+
+def test_mx_equals_nvfp4_with_each_scale_duplicated_per_16():
+    """A power-of-two E8M0 scale that E4M3 also holds (2^-9 .. 2^8), repeated for
+    both 16-groups of its 32-group, gives the same weights in either format."""
+    rng = np.random.default_rng(12)
+    n, k = 16, 256
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    mx = rng.integers(127 - 9, 127 + 9, (n, k // 32), dtype=np.uint8)
+    pow2 = torch.from_numpy(np.ldexp(1.0, mx.astype(np.int64) - 127).astype(np.float32))
+    e4 = pow2.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(torch.from_numpy(e4).view(torch.float8_e4m3fn).double().numpy(), pow2.double().numpy())
+    nv = np.repeat(e4, 2, axis=1)
+    s2 = np.float32(0.75)
+    assert np.array_equal(oracle.dequant(packed, mx, s2, n, k, fmt="mxfp4"),
+                          oracle.dequant(packed, nv, s2, n, k, fmt="nvfp4"))
+
+
+def test_mx_single_expert_equals_dense_swiglu_torch():
+    shape = synth.MoeShape("dense_mx", 5, 128, 64, 1, 1, "uniform", True)
+    x = synth.gen_x(1, shape)
+    ids = np.zeros((5, 1), dtype=np.int32)
+    w = np.ones((5, 1), dtype=np.float32)
+
+    def wf(e, p):
+        pk, sc = synth.gen_expert_mx(1, e, p, shape)
+        return oracle.transpose_u8(pk), oracle.transpose_u8(sc), synth.SCALE2_MX_F32
+
+    res = oracle.moe_layer(x, ids, w, wf, 1, 128, 64, kmajor=True, fmt="mxfp4")
+    Wg, Wu, Wd = (torch.tensor([[_scalar_dequant_mx(*synth.gen_expert_mx(1, 0, p, shape), synth.SCALE2_MX_F32, i, j)
+                                 for j in range(kk)] for i in range(n)], dtype=torch.float64)
+                  for p, (n, kk) in zip((0, 1, 2), ((64, 128), (64, 128), (128, 64))))
+    xt = torch.from_numpy(x.astype(np.int16)).view(torch.bfloat16).double()
+    dense = (F.silu(xt @ Wg.T) * (xt @ Wu.T)) @ Wd.T
+    assert np.allclose(res["out"], dense.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_mx_group_of_16_is_caught():
+    """Negative control: an MXFP4 decode that steps its scale every 16 values
+    (the NVFP4 group) disagrees with the scalar decode the pins use."""
+    rng = np.random.default_rng(13)
+    n, k = 8, 128
+    packed = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    mx = rng.integers(110, 140, (n, k // 32), dtype=np.uint8)
+    kk = np.arange(k)
+    nib = (packed[:, kk >> 1] >> (4 * (kk & 1)).astype(np.uint8)) & 0xF
+    wrong = oracle.E2M1[nib] * oracle.E8M0[mx[:, np.minimum(kk >> 4, k // 32 - 1)]]
+    ref = np.array([[_scalar_dequant_mx(packed, mx, 1.0, i, j) for j in range(k)] for i in range(n)])
+    assert np.array_equal(oracle.dequant(packed, mx, 1.0, n, k, fmt="mxfp4"), ref)
+    assert not np.array_equal(wrong, ref)
+
+
 # ---------------------------------------------------------------- P4: transpose
 def test_transpose_bruteforce_and_involution():
     rng = np.random.default_rng(1)
@@ -383,15 +477,15 @@ def test_null_expert_and_zero_weight_contribute_zero():
 def _mutants():
     good_dequant = om.dequant
 
-    def swapped_nibbles(packed, scale, s2, n, k, kmajor=False):
+    def swapped_nibbles(packed, scale, s2, n, k, kmajor=False, fmt="nvfp4"):
         sw = ((packed & 0xF) << 4) | (packed >> 4)
-        return good_dequant(sw.astype(np.uint8), scale, s2, n, k, kmajor)
+        return good_dequant(sw.astype(np.uint8), scale, s2, n, k, kmajor, fmt)
 
-    def group_off_by_one(packed, scale, s2, n, k, kmajor=False):
-        return good_dequant(packed, np.roll(scale, 1, axis=1 if not kmajor else 0), s2, n, k, kmajor)
+    def group_off_by_one(packed, scale, s2, n, k, kmajor=False, fmt="nvfp4"):
+        return good_dequant(packed, np.roll(scale, 1, axis=1 if not kmajor else 0), s2, n, k, kmajor, fmt)
 
-    def no_scale2(packed, scale, s2, n, k, kmajor=False):
-        return good_dequant(packed, scale, 1.0, n, k, kmajor) * float(synth.SCALE2_F32) * 1.5
+    def no_scale2(packed, scale, s2, n, k, kmajor=False, fmt="nvfp4"):
+        return good_dequant(packed, scale, 1.0, n, k, kmajor, fmt) * float(synth.SCALE2_F32) * 1.5
 
     return {"swapped_nibbles": swapped_nibbles, "group_off_by_one": group_off_by_one, "bad_scale2": no_scale2}
 
