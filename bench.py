@@ -1,6 +1,6 @@
 """Benchmark of the grouped NVFP4 MoE expert projection on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--eager]
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--eager] [--format nvfp4|mxfp4]
 
 A step is one MoE layer forward through the whole path — routing sort,
 gate+up+SiLU, down, blend — over one batch of synthetic input.  Every input
@@ -21,6 +21,8 @@ instead).  Reported on one JSON line:
               matrix-core peak); traffic = HBM bytes per launch from the
               committed counter summary in profiles/ while the kernel sources
               are unchanged since it was taken, else null
+  --format mxfp4 runs the many-token workload with MXFP4 experts (E8M0
+  scales per 32 k) instead of NVFP4; the workload name says so.
   router      launch time of moe_nvfp4_route on the workload's logits (the
               router ahead of the path; not part of the step)
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
@@ -29,6 +31,7 @@ instead).  Reported on one JSON line:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="weight copies cycled over (0 = auto)")
     ap.add_argument("--batches", type=int, default=8, help="distinct routing batches cycled over")
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of one graph")
+    ap.add_argument("--format", choices=["nvfp4", "mxfp4"], default="nvfp4",
+                    help="expert weight format (mxfp4: K-major workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-pass", choices=["gate_up", "copy"], default=None,
@@ -102,22 +107,22 @@ def measured_traffic(workload: str):
         return None
 
 
-def active_weight_bytes(shape, ids) -> int:
+def active_weight_bytes(shape, ids, group: int = 16) -> int:
     import synth
 
     act = np.unique(ids[(ids >= 0) & (ids < shape.E)])
-    return int(act.size) * synth.expert_bytes(shape)
+    return int(act.size) * synth.expert_bytes(shape, group)
 
 
-def gate_up_bytes(shape, ids) -> int:
+def gate_up_bytes(shape, ids, group: int = 16) -> int:
     """Algorithmic bytes of one gate+up launch: the active experts' gate and up
     weights (packed + scales), x read once, h written once, 4-byte scale_2s."""
     act = np.unique(ids[(ids >= 0) & (ids < shape.E)]).size
-    w = act * 2 * (shape.I * shape.H // 2 + shape.I * shape.H // 16 + 4)
+    w = act * 2 * (shape.I * shape.H // 2 + shape.I * shape.H // group + 4)
     return int(w + shape.T * shape.H * 2 + shape.P * shape.I * 4)
 
 
-def cpu_baseline(shape, cfg_id, seconds):
+def cpu_baseline(shape, cfg_id, seconds, fmt="nvfp4"):
     """Time the fp64 oracle on a bounded sample: whole layer forwards of the
     same workload (tokens sampled down for the many-token workload)."""
     import oracle
@@ -134,7 +139,13 @@ def cpu_baseline(shape, cfg_id, seconds):
     sub = synth.MoeShape(shape.name + "_cpu", T, shape.H, shape.I, shape.E, shape.k, shape.routing, False,
                          shape.zipf_s)
 
+    mx = fmt == "mxfp4"
+    group = 32 if mx else 16
+
     def wf(e, proj):
+        if mx:
+            pk, sc = synth.gen_expert_mx(cfg_id, e, proj, shape)
+            return pk, sc, synth.SCALE2_MX_F32
         pk, sc = synth.gen_expert(cfg_id, e, proj, shape)
         return pk, sc, synth.SCALE2_F32
 
@@ -150,10 +161,10 @@ def cpu_baseline(shape, cfg_id, seconds):
             for p in (0, 1, 2):
                 cache[(int(e), p)] = wf(int(e), p)
         t0 = time.perf_counter()
-        oracle.moe_layer(x, ids, w, lambda e, p: cache[(e, p)], sub.E, sub.H, sub.I)
+        oracle.moe_layer(x, ids, w, lambda e, p: cache[(e, p)], sub.E, sub.H, sub.I, fmt=fmt)
         t_used += time.perf_counter() - t0
         done_tokens += T
-        done_bytes += active_weight_bytes(sub, ids)
+        done_bytes += active_weight_bytes(sub, ids, group)
         runs += 1
         b += 1
     return {
@@ -185,7 +196,17 @@ def main():
     dev = torch.device("cuda:0")
     cfg_id = args.workload
     shape = synth.config(cfg_id)
-    layout = moe.K_MAJOR if shape.kmajor else moe.ROW_MAJOR
+    mx = args.format == "mxfp4"
+    if mx and not shape.kmajor:
+        sys.exit("bench.py: --format mxfp4 runs on the K-major (many-token) workload only")
+    group = 32 if mx else 16
+    scale2 = synth.SCALE2_MX_F32 if mx else synth.SCALE2_F32
+    gen = synth.gen_expert_mx if mx else synth.gen_expert
+    if mx:
+        shape = dataclasses.replace(shape, name=shape.name + "_mxfp4")
+        layout = moe.K_MAJOR_MXFP4
+    else:
+        layout = moe.K_MAJOR if shape.kmajor else moe.ROW_MAJOR
 
     # ---- inputs: R routing batches, L layers of expert weights -----------
     R = max(1, args.batches)
@@ -197,8 +218,8 @@ def main():
         ws.append(w)
     ids_d = [torch.from_numpy(i).to(dev) for i in idss]
     w_d = [torch.from_numpy(w).to(dev) for w in ws]
-    step_bytes = [active_weight_bytes(shape, i) for i in idss]
-    all_bytes = shape.E * synth.expert_bytes(shape)
+    step_bytes = [active_weight_bytes(shape, i, group) for i in idss]
+    all_bytes = shape.E * synth.expert_bytes(shape, group)
     if args.layers > 0:
         L = args.layers
     else:
@@ -208,15 +229,15 @@ def main():
     for e in range(shape.E):
         for p in (0, 1, 2):
             n, k = synth.proj_dims(shape, p)
-            pk, sc = synth.gen_expert(cfg_id, e, p, shape)
+            pk, sc = gen(cfg_id, e, p, shape)
             pk_d, sc_d = torch.from_numpy(pk).to(dev), torch.from_numpy(sc).to(dev)
             if shape.kmajor:
-                pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k)
+                pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k, group)
             base[(e, p)] = (pk_d, sc_d)
     layers = []
     for li in range(L):
         wts = base if li == 0 else {key: (a.clone(), b.clone()) for key, (a, b) in base.items()}
-        tabs = [moe.ExpertTables([(wts[(e, p)][0], wts[(e, p)][1], synth.SCALE2_F32) for e in range(shape.E)],
+        tabs = [moe.ExpertTables([(wts[(e, p)][0], wts[(e, p)][1], scale2) for e in range(shape.E)],
                                  layout, device=dev) for p in (0, 1, 2)]
         layers.append((wts, tabs))
     bufs = moe.MoeLayer(shape.T, shape.k, shape.E, shape.H, shape.I, *layers[0][1], device=dev)
@@ -306,7 +327,7 @@ def main():
             e1.record(stream)
     torch.cuda.synchronize()
     gu_ms = e0.elapsed_time(e1) / Kr
-    gu_bytes = float(gate_up_bytes(shape, idss[0]))
+    gu_bytes = float(gate_up_bytes(shape, idss[0], group))
     traffic = measured_traffic(shape.name)
     if shape.kmajor:
         # Many-token path: a dense bf16 contraction on the matrix cores.
@@ -356,6 +377,7 @@ def main():
             "workload": shape.name,
             "tokens": shape.T, "hidden": shape.H, "expert_inter": shape.I, "experts": shape.E, "top_k": shape.k,
             "routing": shape.routing, "weight_layout": "k_major" if shape.kmajor else "row_major",
+            "weight_format": args.format,
             "weight_copies_cycled": L, "routing_batches_cycled": R,
             "launch": "eager" if args.eager else "hip_graph",
         },
@@ -367,7 +389,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(shape, cfg_id, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(shape, cfg_id, args.cpu_seconds, args.format)
     print(json.dumps(line), flush=True)
 
 

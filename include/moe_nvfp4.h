@@ -48,11 +48,12 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 1
+#define MOE_NVFP4_ABI_VERSION 2
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
-#define MOE_NVFP4_ROW_MAJOR 0 /* packed [N, K/2], scales [N, K/16]  (decode GEMV path) */
-#define MOE_NVFP4_K_MAJOR   1 /* packed [K/2, N], scales [K/16, N]  (many-token MFMA path) */
+#define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
+#define MOE_NVFP4_K_MAJOR       1 /* packed [K/2, N], E4M3 scales [K/16, N]  (many-token MFMA path) */
+#define MOE_NVFP4_K_MAJOR_MXFP4 2 /* packed [K/2, N], E8M0 scales [K/32, N]  (many-token MFMA path) */
 
 /* Host-side argument errors (nothing is launched). */
 #define MOE_NVFP4_OK          0
@@ -68,21 +69,28 @@ extern "C" {
  * One NVFP4 projection across the experts (the pages' Nvfp4ExpertTables):
  * device arrays of E device pointers and E floats.
  *   packed[e]  E2M1 nibbles, two per byte, low nibble = even k.
- *              ROW_MAJOR: [N, K/2]; K_MAJOR: [K/2, N].
+ *              ROW_MAJOR: [N, K/2]; K_MAJOR, K_MAJOR_MXFP4: [K/2, N].
  *   scale[e]   E4M3 (OCP "FN": bias 7, max 448, NaN = S.1111.111) block
  *              scales, one per 16 consecutive k.  ROW_MAJOR: [N, K/16];
  *              K_MAJOR: [K/16, N].
- *   scale2[e]  the per-tensor f32 scale_2.
- * Weight element (n, k) = e2m1(nibble) * e4m3(scale of group k/16) * scale_2.
+ *              K_MAJOR_MXFP4: E8M0 block scales (OCP MX: value
+ *              2^(code - 127)), one per 32 consecutive k, [K/32, N]
+ *              (transpose.rs, transpose_for_gemm: native-MXFP4 experts use
+ *              a scale group of 32).
+ *   scale2[e]  the per-tensor f32 scale_2 (1.0 for plain MXFP4).
+ * Weight element (n, k) = e2m1(nibble) * e4m3(scale of group k/16) * scale_2,
+ * or, for K_MAJOR_MXFP4, e2m1(nibble) * e8m0(scale of group k/32) * scale_2.
  * packed[e] == NULL marks an absent expert (not owned under expert
  * parallelism): its rows of h and y are written as 0, so it contributes 0.
- * Scale codes must not be NaN (0x7F, 0xFF): results are then unspecified.
+ * Scale codes must not be NaN (E4M3 0x7F, 0xFF; E8M0 0xFF): results are
+ * then unspecified.  E8M0 codes above 252 can take a weight past the f32
+ * range (it then decodes to infinity).
  */
 typedef struct {
     const uint8_t *const *packed;
     const uint8_t *const *scale;
     const float *scale2;
-    int32_t layout; /* MOE_NVFP4_ROW_MAJOR or MOE_NVFP4_K_MAJOR */
+    int32_t layout; /* MOE_NVFP4_ROW_MAJOR, MOE_NVFP4_K_MAJOR or MOE_NVFP4_K_MAJOR_MXFP4 */
 } moe_nvfp4_experts;
 
 /* Maximum sizes admitted by the calls below. */
@@ -130,19 +138,21 @@ int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
  *   x                 in  bf16 [T, H]
  *   gate, up          NVFP4 tables, N = I, K = H, both in the same layout.
  *                     ROW_MAJOR runs the decode GEMV (few tokens per expert);
- *                     K_MAJOR runs the grouped MFMA GEMM (many tokens).
+ *                     K_MAJOR and K_MAJOR_MXFP4 run the grouped MFMA GEMM
+ *                     (many tokens).
  *   expert_offsets, sorted_token_ids, active_experts, active_count:
  *                     moe_nvfp4_sort's outputs (read on the device only).
  *   h                 out fp32 [P, I]; rows of positions that belong to no
  *                     active expert are left untouched.
  * Admission: H % 64 == 0 and I % 64 == 0 (both layouts), H >= 256 and
  * I >= 256 (ROW_MAJOR); packed, scale and activation buffers 16-byte
- * aligned; K_MAJOR: the activation tensor (x here, h for the down
- * projection) below 4 GiB.  The K_MAJOR path feeds the matrix cores with
+ * aligned; K_MAJOR(_MXFP4): the activation tensor (x here, h for the down
+ * projection) below 4 GiB.  The K-major path feeds the matrix cores with
  * bf16 operands (x as given, the decoded weights exactly), so it admits the
  * whole bf16 range.
- * Errors: ENULL, ESHAPE, ELAYOUT, ELIMIT (E, P or width above the maxima,
- * or a K_MAJOR activation tensor of 4 GiB or more).
+ * Errors: ENULL, ESHAPE, ELAYOUT (unknown layout, or gate and up differ),
+ * ELIMIT (E, P or width above the maxima, or a K-major activation tensor of
+ * 4 GiB or more).
  */
 int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
                            int32_t I, moe_nvfp4_experts gate, moe_nvfp4_experts up,
@@ -159,7 +169,7 @@ int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, i
  *
  *   h      in  fp32 [P, I]   (the kernels round it to 16-bit floats for
  *                             the products; accumulation stays fp32)
- *   down   NVFP4 table, N = H, K = I.
+ *   down   NVFP4 (or, K-major only, MXFP4) table, N = H, K = I.
  *   y      out fp32 [P, H]; rows of positions outside every active expert are
  *          left untouched.
  * Admission and errors as moe_nvfp4_gate_up_silu.
@@ -190,7 +200,7 @@ int moe_nvfp4_blend(const float *y, const float *topk_weights, const int32_t *pa
  * (transpose.rs, transpose_for_gemm_gs and its host loop):
  *     dst[c * rows + r] = src[r * cols + c]     for r < rows, c < cols.
  * Applied to a packed weight with rows = N, cols = K/2 and to its scales
- * with rows = N, cols = K/16, it builds the K_MAJOR twin.  src is left
+ * with rows = N, cols = K/16 (MXFP4: K/32), it builds the K-major twin.  src is left
  * unchanged; src and dst must not overlap.
  * Errors: ENULL; ESHAPE if rows < 1 or cols < 1; ELIMIT if rows * cols
  * exceeds 2^40 bytes.

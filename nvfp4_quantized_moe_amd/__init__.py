@@ -28,6 +28,7 @@ __all__ = [
     "MoeNvfp4Error",
     "ROW_MAJOR",
     "K_MAJOR",
+    "K_MAJOR_MXFP4",
     "FLAG_BAD_EXPERT_ID",
     "lib",
     "header_functions",
@@ -43,6 +44,7 @@ __all__ = [
 
 ROW_MAJOR = 0
 K_MAJOR = 1
+K_MAJOR_MXFP4 = 2  # K-major MXFP4: E8M0 scales, one per 32 k
 FLAG_BAD_EXPERT_ID = 1
 
 _PKG = pathlib.Path(__file__).resolve().parent
@@ -127,9 +129,10 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
 
 
 class ExpertTables:
-    """One NVFP4 projection across E experts: device arrays of the experts'
-    packed and scale pointers plus their f32 scale_2 values.  ``None`` in
-    ``weights`` marks an absent (NULL) expert."""
+    """One projection across E experts: device arrays of the experts' packed
+    and scale pointers plus their f32 scale_2 values, in one of the layouts
+    ROW_MAJOR, K_MAJOR (NVFP4) or K_MAJOR_MXFP4.  ``None`` in ``weights``
+    marks an absent (NULL) expert."""
 
     def __init__(self, weights: Sequence[Optional[tuple]], layout: int, device="cuda"):
         packed, scales, s2 = [], [], []

@@ -1,19 +1,19 @@
 // C-ABI entry points of the two projection steps: host-side argument checks,
 // then one launch on the caller's stream.  The weight layout picks the
-// kernel: row-major -> decode kernel (few rows per expert), K-major -> grouped
-// MFMA GEMM (many rows per expert), mirroring the pages' split between the
-// row-major decode kernels (nvfp4_moe_grouped.rs) and the transposed twins
-// built for the sorted prefill path (prefill_weights.rs).
+// kernel: row-major -> decode kernel (few rows per expert), K-major (NVFP4 or
+// MXFP4) -> grouped MFMA GEMM (many rows per expert), mirroring the pages'
+// split between the row-major decode kernels (nvfp4_moe_grouped.rs) and the
+// transposed twins built for the sorted prefill path (prefill_weights.rs).
 #include "moe_common.hpp"
 
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
                           hipStream_t stream);
-int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
-                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
-                           const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
-                           hipStream_t stream);
+int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *sorted_tok,
+                           const int32_t *offsets, const int32_t *active, const int32_t *nactive,
+                           const moe_nvfp4_experts &A, const moe_nvfp4_experts *B, float *out, int N, int K,
+                           int P, int E, hipStream_t stream);
 
 namespace {
 
@@ -21,7 +21,8 @@ int check_common(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I, int32_t 
     if (T < 1 || k < 1 || E < 1 || k > E || H < 1 || I < 1) return MOE_NVFP4_ESHAPE;
     if (E > MOE_NVFP4_MAX_EXPERTS || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
     if (H > MOE_NVFP4_MAX_WIDTH || I > MOE_NVFP4_MAX_WIDTH) return MOE_NVFP4_ELIMIT;
-    if (layout != MOE_NVFP4_ROW_MAJOR && layout != MOE_NVFP4_K_MAJOR) return MOE_NVFP4_ELAYOUT;
+    if (layout != MOE_NVFP4_ROW_MAJOR && layout != MOE_NVFP4_K_MAJOR && layout != MOE_NVFP4_K_MAJOR_MXFP4)
+        return MOE_NVFP4_ELAYOUT;
     if (H % 64 != 0 || I % 64 != 0) return MOE_NVFP4_ESHAPE;
     if (layout == MOE_NVFP4_ROW_MAJOR && (H < 256 || I < 256)) return MOE_NVFP4_ESHAPE;
     return MOE_NVFP4_OK;
@@ -45,8 +46,9 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
         return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
                                      gate, &up, h, I, H, T, P, E, (hipStream_t)stream);
     if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
-    return moe_launch_gemm_kmajor(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
-                                  &up, h, I, H, P, E, (hipStream_t)stream);
+    return moe_launch_gemm_kmajor(true, gate.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
+                                  expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E,
+                                  (hipStream_t)stream);
 }
 
 extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
@@ -62,6 +64,7 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
         return moe_launch_decode_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
                                      nullptr, y, H, I, T, P, E, (hipStream_t)stream);
     if ((uint64_t)P * I * 4 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
-    return moe_launch_gemm_kmajor(false, h, nullptr, expert_offsets, active_experts, active_count, down,
-                                  nullptr, y, H, I, P, E, (hipStream_t)stream);
+    return moe_launch_gemm_kmajor(false, down.layout == MOE_NVFP4_K_MAJOR_MXFP4, h, nullptr, expert_offsets,
+                                  active_experts, active_count, down, nullptr, y, H, I, P, E,
+                                  (hipStream_t)stream);
 }

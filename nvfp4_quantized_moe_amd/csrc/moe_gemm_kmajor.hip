@@ -1,6 +1,7 @@
 // Many-token path: grouped NVFP4 GEMM on the matrix cores, reading the
 // K-major transposed twin of each expert weight (packed [K/2, N], scales
-// [K/16, N]; transpose.rs, transpose_for_gemm, and prefill_weights.rs,
+// [K/16, N], or for MXFP4 experts E8M0 scales [K/32, N]; transpose.rs,
+// transpose_for_gemm and transpose_for_gemm_gs, and prefill_weights.rs,
 // prepare_prefill_weights, which builds these twins for the sorted prefill
 // path).  Same operation as the decode GEMV: gate+up with the fused SiLU
 // product (h fp32 [P, I]) or down (y fp32 [P, H]) over each active expert's
@@ -74,32 +75,46 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Weight decode: E2M1 pairs through the f32 converter (scale 1: the hardware
-// applies only the scale's exponent), times the E4M3 block scale in f32, then
-// rounded to bf16 (exact: at most 6 significant bits).
+// Weight decode.  NVFP4: E2M1 pairs through the f32 converter (scale 1: the
+// hardware applies only the scale's exponent), times the E4M3 block scale in
+// f32, then rounded to bf16 (exact: at most 6 significant bits).  MXFP4: the
+// E8M0 scale is a power of two, i.e. exactly the exponent the converter
+// applies, so one instruction turns two E2M1 codes into scaled bf16 (exact
+// up to the f32 range: E8M0 codes up to 252).
 // ---------------------------------------------------------------------------
 struct Scales4 {
     float v[4];
 };
-// E4M3 block scales of the 4 columns in a scale dword.
+// Block scales of the 4 columns in a scale dword: E4M3 codes widened to f32,
+// or E8M0 codes placed in the exponent field of an f32 (the converter reads
+// that field alone, so code 0 gives 2^-127 and code 255 NaN, as E8M0 defines).
+template <bool MX>
 __device__ __forceinline__ Scales4 scales4(uint32_t s) {
-    return Scales4{{moe::e4m3_f32<0>(s), moe::e4m3_f32<1>(s), moe::e4m3_f32<2>(s), moe::e4m3_f32<3>(s)}};
+    if constexpr (MX)
+        return Scales4{{__uint_as_float((s & 0xffu) << 23), __uint_as_float(((s >> 8) & 0xffu) << 23),
+                        __uint_as_float(((s >> 16) & 0xffu) << 23), __uint_as_float((s >> 24) << 23)}};
+    else
+        return Scales4{{moe::e4m3_f32<0>(s), moe::e4m3_f32<1>(s), moe::e4m3_f32<2>(s), moe::e4m3_f32<3>(s)}};
 }
 
 // One element pair u = 4r + j: packed row r, column 4c+j (byte j).  Called
 // from fully unrolled loops, where u folds to a constant.
-template <int J>
+template <bool MX, int J>
 __device__ __forceinline__ bf16x2_t decode_pair(uint32_t w, float sc) {
-    return __builtin_convertvector(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J) * sc, bf16x2_t);
+    if constexpr (MX)
+        return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, J);
+    else
+        return __builtin_convertvector(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J) * sc, bf16x2_t);
 }
+template <bool MX>
 __device__ __forceinline__ void decode_pair_at(int u, const uint32_t (&w)[4], const Scales4 &sc, bf16x8_t (&b)[4]) {
     const int r = u >> 2, j = u & 3;
     bf16x2_t pr;
     switch (j) {
-        case 0: pr = decode_pair<0>(w[r], sc.v[0]); break;
-        case 1: pr = decode_pair<1>(w[r], sc.v[1]); break;
-        case 2: pr = decode_pair<2>(w[r], sc.v[2]); break;
-        default: pr = decode_pair<3>(w[r], sc.v[3]); break;
+        case 0: pr = decode_pair<MX, 0>(w[r], sc.v[0]); break;
+        case 1: pr = decode_pair<MX, 1>(w[r], sc.v[1]); break;
+        case 2: pr = decode_pair<MX, 2>(w[r], sc.v[2]); break;
+        default: pr = decode_pair<MX, 3>(w[r], sc.v[3]); break;
     }
     b[j][2 * r] = pr.x;
     b[j][2 * r + 1] = pr.y;
@@ -107,14 +122,15 @@ __device__ __forceinline__ void decode_pair_at(int u, const uint32_t (&w)[4], co
 
 // All 4 packed rows of a step (8 consecutive k of columns 4c..4c+3) into the
 // B operands of the 4 interleaved column tiles.
+template <bool MX>
 __device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf16x8_t (&b)[4]) {
-    const Scales4 sc = scales4(s);
+    const Scales4 sc = scales4<MX>(s);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const bf16x2_t p0 = decode_pair<0>(w[r], sc.v[0]);
-        const bf16x2_t p1 = decode_pair<1>(w[r], sc.v[1]);
-        const bf16x2_t p2 = decode_pair<2>(w[r], sc.v[2]);
-        const bf16x2_t p3 = decode_pair<3>(w[r], sc.v[3]);
+        const bf16x2_t p0 = decode_pair<MX, 0>(w[r], sc.v[0]);
+        const bf16x2_t p1 = decode_pair<MX, 1>(w[r], sc.v[1]);
+        const bf16x2_t p2 = decode_pair<MX, 2>(w[r], sc.v[2]);
+        const bf16x2_t p3 = decode_pair<MX, 3>(w[r], sc.v[3]);
         b[0][2 * r] = p0.x;
         b[0][2 * r + 1] = p0.y;
         b[1][2 * r] = p1.x;
@@ -257,6 +273,7 @@ constexpr int kExRows = 16;                  // epilogue exchange: rows per roun
 static_assert(kRowsG * 4 % 64 == 0, "whole wave-wide direct loads");
 static_assert(kExRows * 128 * 4 <= kStageG, "exchange fits in one activation buffer");
 
+template <bool MX>  // MXFP4 weights (E8M0 scales per 32 k) instead of NVFP4
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_gate_up(GemmArgs a) {
     // One LDS array per ring stage: alias analysis then tells the compiler's
     // wait insertion which direct loads an LDS read depends on (with one
@@ -337,16 +354,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // chunk l & 3; it lands at byte 16 l, so row 4 q + r of the step sits at
     // byte 256 r + 64 q and the dword of columns 4c..4c+3 at + 4c: a lane's
     // four rows are 256 bytes apart and each read of 64 lanes touches 64
-    // distinct banks.  Scales: lane l (mod 32) loads the dword of row
-    // (l >> 4) & 1, columns 4 (l & 15) .. +3.
+    // distinct banks.  Scales: lane l (mod 32) loads the dword of the step's
+    // scale row (l >> 4) & 1 (NVFP4: two groups of 16 k; MXFP4: its one
+    // group of 32 k, loaded twice), columns 4 (l & 15) .. +3.
     const int bt = lane >> 2;
     const uint32_t bdoff = (uint32_t)(4 * (bt & 3) + (bt >> 2)) * N + n_ld + 16 * (lane & 3);
-    const uint32_t sdoff = (uint32_t)((lane >> 4) & 1) * N + n_ld + 4 * (lane & 15);
+    constexpr int kSRows = MX ? 1 : 2;  // scale rows per 32-k step
+    const uint32_t sdoff = (uint32_t)(MX ? 0 : (lane >> 4) & 1) * N + n_ld + 4 * (lane & 15);
     auto dma_b = [&](int s, auto st) {
         const int sc_ = s < S ? s : S - 1;
         __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(pk + (size_t)(16 * sc_) * N + bdoff),
                                          (MOE_LDS void *)(wbuf(st) + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(sk + (size_t)(2 * sc_) * N + sdoff),
+        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(sk + (size_t)(kSRows * sc_) * N + sdoff),
                                          (MOE_LDS void *)(wbuf(st) + 4096 + wave * 256), 4, 0, 0);
     };
     const int brd = wave * 1024 + 64 * q + 4 * c, srd = 4096 + wave * 256 + 4 * (16 * (q >> 1) + c);
@@ -394,7 +413,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         dma_a(s + 3, Sn{});
         dma_b(s + 3, Sn{});
         read_b(slot, bw, bsv);
-        decode_b(bw, bsv, bop);
+        decode_b<MX>(bw, bsv, bop);
         const uint8_t *ab = abuf(slot) + aoffs;
         // Row-tile operands are read two tiles ahead.
         bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab);
@@ -484,6 +503,7 @@ constexpr int kChunksD = kRowsD * 4;       // 16-byte (8 k) chunks per step
 constexpr int kSlotsD = kChunksD / kThreads;
 static_assert(kChunksD % kThreads == 0, "whole chunk slots");
 
+template <bool MX>  // MXFP4 weights (E8M0 scales per 32 k) instead of NVFP4
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_down(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageD];
 
@@ -508,7 +528,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n_ld = wact ? n_w : N - 64;
     // Per-lane byte offsets (32-bit) from wave-uniform bases.
     const uint32_t boff = (uint32_t)(4 * q) * N + n_ld + 4 * c;
-    const uint32_t soff = (uint32_t)(q >> 1) * N + n_ld + 4 * c;
+    // Scale row of k-octet q within a 32-k step: NVFP4 has two (groups of 16), MXFP4 one.
+    constexpr int kSRows = MX ? 1 : 2;
+    const uint32_t soff = (uint32_t)(MX ? 0 : q >> 1) * N + n_ld + 4 * c;
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
 
@@ -547,7 +569,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const uint8_t *p = pk + (size_t)(16 * s) * N;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = gload<uint32_t>(p + (size_t)r * N + boff);
-        sv = gload<uint32_t>(sk + (size_t)(2 * s) * N + soff);
+        sv = gload<uint32_t>(sk + (size_t)(kSRows * s) * N + soff);
     };
 
     f32x4_t acc[kMTD][4];
@@ -563,7 +585,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int d = 0; d < kBDist; ++d) load_b(d, bw[d], bs[d]);
     load_a(0);
     store_a(0);
-    decode_b(bw[0], bs[0], bop[0]);
+    decode_b<MX>(bw[0], bs[0], bop[0]);
     load_b(kBDist, bw[0], bs[0]);
     __syncthreads();
 
@@ -580,7 +602,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const bool more = s + 1 < S;
         if (more) load_a(s + 1);
         const uint8_t *ab = abase + p * kStageD;
-        const Scales4 scn = scales4(bs[dn]);
+        const Scales4 scn = scales4<MX>(bs[dn]);
         // Hand-ordered: row-tile operands are read two tiles ahead, and one
         // element pair of the next step's decode (4 VALU) follows every other
         // MFMA.  Full scheduling fences keep this order; the empty asm after
@@ -597,7 +619,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[p][j], acc[i][j], 0, 0, 0);
                 const int m = 4 * i + j;  // MFMA index in the step
                 if ((m & 1) == 0 && m / 2 < 16) {
-                    decode_pair_at(m / 2, bw[dn], scn, bop[p ^ 1]);
+                    decode_pair_at<MX>(m / 2, bw[dn], scn, bop[p ^ 1]);
                     asm volatile("" : "+v"(bop[p ^ 1][0]), "+v"(bop[p ^ 1][1]), "+v"(bop[p ^ 1][2]), "+v"(bop[p ^ 1][3]));
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -641,10 +663,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 }  // namespace
 
-int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
-                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
-                           const moe_nvfp4_experts *B, float *out, int N, int K, int P, int E,
-                           hipStream_t stream) {
+int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *sorted_tok,
+                           const int32_t *offsets, const int32_t *active, const int32_t *nactive,
+                           const moe_nvfp4_experts &A, const moe_nvfp4_experts *B, float *out, int N, int K,
+                           int P, int E, hipStream_t stream) {
     GemmArgs a;
     a.act = act;
     a.sorted_tok = sorted_tok;
@@ -669,9 +691,14 @@ int moe_launch_gemm_kmajor(bool gated, const void *act, const int32_t *sorted_to
     const long long units = mt_bound * a.n_ct;
     const long long grid = ((units + 7) / 8) * 8;
     if (grid > 0x7fffffffLL) return MOE_NVFP4_ELIMIT;
-    if (gated)
-        hipLaunchKernelGGL(k_gemm_gate_up, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    const dim3 g((unsigned)grid), b(kThreads);
+    if (gated && mx)
+        hipLaunchKernelGGL(k_gemm_gate_up<true>, g, b, 0, stream, a);
+    else if (gated)
+        hipLaunchKernelGGL(k_gemm_gate_up<false>, g, b, 0, stream, a);
+    else if (mx)
+        hipLaunchKernelGGL(k_gemm_down<true>, g, b, 0, stream, a);
     else
-        hipLaunchKernelGGL(k_gemm_down, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_gemm_down<false>, g, b, 0, stream, a);
     return moe_host::launch_status();
 }

@@ -23,9 +23,10 @@ Value distributions (one per input, stated by the workload definitions):
     (FN variant) code by torch's float8_e4m3fn cast, ties to even;
   * per-tensor scale_2 = float32(1 / (448 * 6)) for every projection;
   * MXFP4 weights (the many-token shape with native-MXFP4 experts): the
-    same packed bytes; E8M0 scale codes uniform over the integers
-    112..118 (scales 2^-15 .. 2^-9, the magnitude range of the NVFP4
-    weights above: E4M3 scales in [2^-4, 2^2] times 1/2688 ~ 2^-11.4);
+    same packed bytes; block scales drawn as for NVFP4 (a real
+    ``u ~ U[2^-4, 2^2]``) times 2^-11 (the magnitude NVFP4's scale_2 of
+    1/2688 ~ 2^-11.4 gives), rounded to the nearest power of two in log2
+    (E8M0 holds powers of two only): codes 112..118, most of them 116..118;
     scale_2 = 1 (MXFP4 has no per-tensor scale);
   * x: standard normal float32, rounded to bf16 (nearest-even) by torch;
   * router: standard-normal logits (plus, for the skewed workload, a Zipf
@@ -91,12 +92,13 @@ def proj_dims(shape: MoeShape, proj: int) -> tuple[int, int]:
     raise ValueError(proj)
 
 
-def expert_bytes(shape: MoeShape) -> int:
-    """Weight bytes of one expert: packed K/2 + scale K/16 bytes per row, 3 projections."""
+def expert_bytes(shape: MoeShape, group: int = 16) -> int:
+    """Weight bytes of one expert: packed K/2 + scale K/group bytes per row
+    (group 16 for NVFP4, 32 for MXFP4), 3 projections."""
     tot = 0
     for proj in (PROJ_GATE, PROJ_UP, PROJ_DOWN):
         n, k = proj_dims(shape, proj)
-        tot += n * (k // 2) + n * (k // 16)
+        tot += n * (k // 2) + n * (k // group)
     return tot
 
 
@@ -158,5 +160,6 @@ def gen_expert_mx(cfg_id: int, e: int, proj: int, shape: MoeShape | None = None)
     shape = shape or config(cfg_id)
     n, k = proj_dims(shape, proj)
     packed = _rng(cfg_id, 4, e, proj).integers(0, 256, size=(n, k // 2), dtype=np.uint8)
-    scale = _rng(cfg_id, 6, e, proj).integers(112, 119, size=(n, k // 32), dtype=np.uint8)
+    u = _rng(cfg_id, 6, e, proj).uniform(2.0 ** -4, 4.0, size=(n, k // 32))
+    scale = (127 - 11 + np.floor(np.log2(u) + 0.5)).astype(np.uint8)
     return packed, scale

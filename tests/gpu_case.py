@@ -1,7 +1,7 @@
 """Device-side test cases built from the seeded generators.
 
-A ``Case`` uploads one workload's inputs (x, routing, the experts' NVFP4
-weights) to the GPU, builds the pointer tables, and runs the four C-ABI
+A ``Case`` uploads one workload's inputs (x, routing, the experts' NVFP4 or
+MXFP4 weights) to the GPU, builds the pointer tables, and runs the four C-ABI
 calls through ``MoeLayer``.  The oracle side regenerates any expert's bytes
 from the same seeds on the CPU (``weight_fn``), so only what a check needs is
 ever dequantised.
@@ -24,11 +24,18 @@ def say(*a):
 
 class Case:
     def __init__(self, cfg_id: int, shape: synth.MoeShape | None = None, nulls=(), kmajor: bool | None = None,
-                 ids: np.ndarray | None = None, weights: np.ndarray | None = None, all_experts: bool = False):
+                 ids: np.ndarray | None = None, weights: np.ndarray | None = None, all_experts: bool = False,
+                 fmt: str = "nvfp4", gen=None):
         self.cfg_id = cfg_id
         self.shape = shape or synth.config(cfg_id)
         s = self.shape
         self.kmajor = s.kmajor if kmajor is None else kmajor
+        # Weight format: NVFP4 (E4M3 per 16) or MXFP4 (E8M0 per 32, K-major only).
+        self.fmt = fmt
+        mx = fmt == "mxfp4"
+        assert not mx or self.kmajor
+        self.gen = gen or (synth.gen_expert_mx if mx else synth.gen_expert)
+        group = 32 if mx else 16
         self.x_bits = synth.gen_x(cfg_id, s)
         gids, gw = synth.gen_routing(cfg_id, s)
         self.ids = gids if ids is None else ids.astype(np.int32)
@@ -43,15 +50,15 @@ class Case:
                 continue
             for proj in (0, 1, 2):
                 n, k = synth.proj_dims(s, proj)
-                pk, sc = synth.gen_expert(cfg_id, e, proj, s)
+                pk, sc = self.gen(cfg_id, e, proj, s)
                 pk_d = torch.from_numpy(pk).cuda()
                 sc_d = torch.from_numpy(sc).cuda()
                 if self.kmajor:
-                    pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k)
+                    pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k, group)
                 self.dev[(e, proj)] = (pk_d, sc_d)
-        layout = moe.K_MAJOR if self.kmajor else moe.ROW_MAJOR
-        self.scale2 = {p: np.float32(synth.SCALE2_F32) for p in (0, 1, 2)}
-        self.tables = [self._table(p, layout) for p in (0, 1, 2)]
+        s2 = synth.SCALE2_MX_F32 if mx else synth.SCALE2_F32
+        self.scale2 = {p: np.float32(s2) for p in (0, 1, 2)}
+        self.tables = [self._table(p, self.layout) for p in (0, 1, 2)]
         self.x = torch.from_numpy(self.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
         self.ids_d = torch.from_numpy(self.ids).cuda()
         self.w_d = torch.from_numpy(self.w).cuda()
@@ -64,10 +71,15 @@ class Case:
             rows.append(None if t is None else (t[0], t[1], self.scale2[proj]))
         return moe.ExpertTables(rows, layout)
 
+    @property
+    def layout(self) -> int:
+        if self.fmt == "mxfp4":
+            return moe.K_MAJOR_MXFP4
+        return moe.K_MAJOR if self.kmajor else moe.ROW_MAJOR
+
     def set_scale2(self, proj: int, value: float):
         self.scale2[proj] = np.float32(value)
-        layout = moe.K_MAJOR if self.kmajor else moe.ROW_MAJOR
-        self.tables[proj] = self._table(proj, layout)
+        self.tables[proj] = self._table(proj, self.layout)
         self.layer.gate, self.layer.up, self.layer.down = self.tables
 
     # oracle-side weights (row-major numpy, regenerated from the seeds)
@@ -77,7 +89,7 @@ class Case:
         def fn(e, proj):
             if e in self.nulls:
                 return None
-            pk, sc = synth.gen_expert(self.cfg_id, e, proj, s)
+            pk, sc = self.gen(self.cfg_id, e, proj, s)
             return pk, sc, self.scale2[proj]
 
         return fn

@@ -19,7 +19,7 @@ def test_library_exports_every_header_function():
                           "transpose_u8", "moe_nvfp4_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 1
+    assert L.moe_nvfp4_abi_version() == 2
 
 
 def _ex(layout=0, null=False):
@@ -50,7 +50,9 @@ def test_gate_up_rejects():
     assert call(h=None) == ENULL
     assert call(g=_ex(null=True)) == ENULL
     assert call(g=_ex(0), u=_ex(1)) == ELAYOUT
+    assert call(g=_ex(1), u=_ex(2)) == ELAYOUT          # NVFP4 gate with MXFP4 up
     assert call(g=_ex(7), u=_ex(7)) == ELAYOUT
+    assert call(g=_ex(3), u=_ex(3)) == ELAYOUT
     assert call(H=48) == ESHAPE                         # H % 64 != 0
     assert call(H=96) == ESHAPE                         # H % 64 != 0
     assert call(H=192) == ESHAPE                        # row-major needs H >= 256
@@ -59,6 +61,8 @@ def test_gate_up_rejects():
     assert call(H=1 << 17) == ELIMIT
     # K-major: x of 4 GiB or more (activation offsets are 32-bit)
     assert call(T=1 << 16, H=1 << 15, g=_ex(1), u=_ex(1)) == ELIMIT
+    assert call(T=1 << 16, H=1 << 15, g=_ex(2), u=_ex(2)) == ELIMIT
+    assert call(I=528, g=_ex(2), u=_ex(2)) == ESHAPE
 
 
 def test_down_and_blend_and_transpose_reject():
@@ -68,6 +72,8 @@ def test_down_and_blend_and_transpose_reject():
     assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 500, _ex(), D, D, D, D, None) == ESHAPE
     # K-major: h of 4 GiB or more
     assert L.moe_nvfp4_down(D, 1 << 20, 4, 4, 256, 1024, _ex(1), D, D, D, D, None) == ELIMIT
+    assert L.moe_nvfp4_down(D, 1 << 20, 4, 4, 256, 1024, _ex(2), D, D, D, D, None) == ELIMIT
+    assert L.moe_nvfp4_down(D, 4, 2, 4, 256, 512, _ex(4), D, D, D, D, None) == ELAYOUT
     assert L.moe_nvfp4_blend(D, D, None, 4, 2, 256, D, None) == ENULL
     assert L.moe_nvfp4_blend(D, D, D, 0, 2, 256, D, None) == ESHAPE
     assert L.moe_nvfp4_blend(D, D, D, 4, 2, 1 << 17, D, None) == ELIMIT

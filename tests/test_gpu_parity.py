@@ -35,7 +35,8 @@ def _check_sort(case, ref):
 def _full_check(case, tag):
     s = case.shape
     case.run()
-    ref = oracle.moe_layer(case.x_bits, case.ids, case.w, case.weight_fn(), s.E, s.H, s.I, kmajor=False)
+    ref = oracle.moe_layer(case.x_bits, case.ids, case.w, case.weight_fn(), s.E, s.H, s.I, kmajor=False,
+                           fmt=case.fmt)
     _check_sort(case, ref)
     n = int(ref["expert_offsets"][-1])
     eh = parity.assert_parity(_h2f(case.layer.h)[:n], ref["h"][:n], f"{tag} h")
@@ -381,3 +382,51 @@ def test_shared_expert_in_the_same_launches(kmajor):
     assert np.array_equal(aug_w[:, :-1], w) and np.all(aug_w[:, -1] == 1.0)
     shape = synth.MoeShape("shared3", base.T, base.H, base.I, base.E + 1, base.k + 1, "zipf", kmajor)
     _full_check(Case(3, shape, ids=aug_ids, weights=aug_w), f"shared {kmajor}")
+
+
+# ---------------------------------------------------------------- MXFP4 experts (next step F3)
+def test_layer_prefill_kmajor_mxfp4_full():
+    """The many-token workload (2048 tokens, H=4096, I=1536, E=64, top-4) with
+    MXFP4 experts: K-major twins with one E8M0 scale per 32 k."""
+    say("layer cfg 5 shape, MXFP4 experts")
+    _full_check(Case(5, fmt="mxfp4"), "cfg5 mxfp4")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(5, 576, 448, 3, 2), (130, 256, 320, 4, 2), (37, 1216, 704, 5, 3),
+                                        (300, 128, 64, 2, 2)])
+def test_ragged_shapes_mxfp4(T, H, I, E, k):
+    say("ragged mxfp4", T, H, I, E, k)
+    shape = synth.MoeShape(f"ragged_mx_{T}_{H}_{I}_{E}_{k}", T, H, I, E, k, "uniform", True)
+    _full_check(Case(21, shape, fmt="mxfp4"), f"ragged mxfp4 {T},{H},{I},{E},{k}")
+
+
+def test_mxfp4_null_expert_and_scale_range():
+    """E8M0 codes over 2^-60 .. 2^20 (gate, up) and 2^-30 .. 2^10 (down), one
+    NULL expert.  Here the output columns, not the rows, differ by orders of
+    magnitude (each weight row has its own scale codes), so the strict rule
+    is applied with each column rescaled to unit RMS."""
+    shape = synth.MoeShape("mx_range", 96, 256, 192, 3, 2, "uniform", True)
+
+    def gen(cfg_id, e, proj, s):
+        pk, _ = synth.gen_expert_mx(cfg_id, e, proj, s)
+        n, kk = synth.proj_dims(s, proj)
+        lo, hi = (67, 147) if proj < 2 else (97, 137)
+        sc = np.random.default_rng([cfg_id, e, proj, 99]).integers(lo, hi + 1, (n, kk // 32), dtype=np.uint8)
+        return pk, sc
+
+    case = Case(22, shape, nulls=(1,), fmt="mxfp4", gen=gen)
+    case.run()
+    ref = oracle.moe_layer(case.x_bits, case.ids, case.w, case.weight_fn(), 3, 256, 192, fmt="mxfp4")
+    _check_sort(case, ref)
+    n = int(ref["expert_offsets"][-1])
+    for name, got, want in (("h", _h2f(case.layer.h)[:n], ref["h"][:n]), ("y", _h2f(case.layer.y)[:n], ref["y"][:n])):
+        for e in ref["active_experts"][: ref["active_count"]]:
+            lo, hi = int(ref["expert_offsets"][e]), int(ref["expert_offsets"][e + 1])
+            g, w = got[lo:hi], want[lo:hi]
+            if e == 1:
+                assert np.array_equal(g, np.zeros_like(g)), "NULL expert rows"
+                continue
+            col = np.sqrt(np.mean(w * w, axis=0))
+            rel = np.abs(g - w) / (col + np.abs(w) + 1e-300)
+            assert rel.max() <= 1e-2, (name, int(e), float(rel.max()))
+    say("mx range ok", float(np.abs(ref["h"][:n]).max()), float(np.abs(ref["h"][:n][ref["h"][:n] != 0]).min()))
