@@ -1,6 +1,7 @@
 """Benchmark of the grouped NVFP4 MoE expert projection on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 2] [--eager] [--format nvfp4|mxfp4]
+                    [--gate-up separate|concat]
 
 A step is one MoE layer forward through the whole path — routing sort,
 gate+up+SiLU, down, blend — over one batch of synthetic input.  Every input
@@ -22,7 +23,8 @@ instead).  Reported on one JSON line:
               committed counter summary in profiles/ while the kernel sources
               are unchanged since it was taken, else null
   --format mxfp4 runs the many-token workload with MXFP4 experts (E8M0
-  scales per 32 k) instead of NVFP4; the workload name says so.
+  scales per 32 k) instead of NVFP4; --gate-up concat runs its gate+up over
+  one concatenated gate||up twin per expert; the workload name says so.
   router      launch time of moe_nvfp4_route on the workload's logits (the
               router ahead of the path; not part of the step)
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of one graph")
     ap.add_argument("--format", choices=["nvfp4", "mxfp4"], default="nvfp4",
                     help="expert weight format (mxfp4: K-major workloads only)")
+    ap.add_argument("--gate-up", choices=["separate", "concat"], default="separate",
+                    help="gate and up as two K-major twins, or one concatenated twin (K-major workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-pass", choices=["gate_up", "copy"], default=None,
@@ -202,11 +206,16 @@ def main():
     group = 32 if mx else 16
     scale2 = synth.SCALE2_MX_F32 if mx else synth.SCALE2_F32
     gen = synth.gen_expert_mx if mx else synth.gen_expert
+    concat = args.gate_up == "concat"
+    if concat and not shape.kmajor:
+        sys.exit("bench.py: --gate-up concat runs on the K-major (many-token) workload only")
     if mx:
         shape = dataclasses.replace(shape, name=shape.name + "_mxfp4")
         layout = moe.K_MAJOR_MXFP4
     else:
         layout = moe.K_MAJOR if shape.kmajor else moe.ROW_MAJOR
+    if concat:
+        shape = dataclasses.replace(shape, name=shape.name + "_concat")
 
     # ---- inputs: R routing batches, L layers of expert weights -----------
     R = max(1, args.batches)
@@ -234,13 +243,36 @@ def main():
             if shape.kmajor:
                 pk_d, sc_d = moe.transpose_for_gemm(pk_d, sc_d, n, k, group)
             base[(e, p)] = (pk_d, sc_d)
+    pitch = 0
+    if concat:
+        for e in range(shape.E):
+            parts = [(torch.from_numpy(pk).to(dev), torch.from_numpy(sc).to(dev), shape.I)
+                     for pk, sc in (gen(cfg_id, e, p, shape) for p in (0, 1))]
+            pt, st, pitch = moe.transpose_concat_for_gemm(parts, shape.H, group, align=16)
+            base[(e, "gu")] = (pt, st)
     layers = []
     for li in range(L):
         wts = base if li == 0 else {key: (a.clone(), b.clone()) for key, (a, b) in base.items()}
         tabs = [moe.ExpertTables([(wts[(e, p)][0], wts[(e, p)][1], scale2) for e in range(shape.E)],
                                  layout, device=dev) for p in (0, 1, 2)]
-        layers.append((wts, tabs))
-    bufs = moe.MoeLayer(shape.T, shape.k, shape.E, shape.H, shape.I, *layers[0][1], device=dev)
+        gu = None
+        if concat:
+            gu = moe.ExpertTables([(wts[(e, "gu")][0], wts[(e, "gu")][1], scale2) for e in range(shape.E)],
+                                  layout, device=dev)
+        layers.append((wts, tabs, gu))
+    bufs = moe.MoeLayer(shape.T, shape.k, shape.E, shape.H, shape.I, *layers[0][1], device=dev,
+                        gate_up=layers[0][2], pitch=pitch)
+
+    def gate_up_launch(li, s):
+        tabs, gu = layers[li % L][1], layers[li % L][2]
+        if gu is not None:
+            moe.moe_nvfp4_gate_up_silu_concat(xs[0], shape.k, shape.E, shape.H, shape.I, gu, pitch,
+                                              bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
+                                              bufs.active_count, bufs.h, s)
+        else:
+            moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
+                                       bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
+                                       bufs.active_count, bufs.h, s)
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -258,15 +290,13 @@ def main():
             moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
                                bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
             for i in range(args.steps):
-                tabs = layers[i % L][1]
-                moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
-                                           bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
-                                           bufs.active_count, bufs.h, stream)
+                gate_up_launch(i, stream)
         torch.cuda.synchronize()
         return
 
     def step(i, s):
         bufs.gate, bufs.up, bufs.down = layers[i % L][1]
+        bufs.gate_up = layers[i % L][2]
         b = i % R
         bufs.forward(xs[b], ids_d[b], w_d[b], stream=s)
 
@@ -320,10 +350,7 @@ def main():
         for rep in range(2):  # the first pass warms the launch path
             e0.record(stream)
             for i in range(Kr):
-                tabs = layers[i % L][1]
-                moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
-                                           bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
-                                           bufs.active_count, bufs.h, stream)
+                gate_up_launch(i, stream)
             e1.record(stream)
     torch.cuda.synchronize()
     gu_ms = e0.elapsed_time(e1) / Kr
@@ -377,7 +404,7 @@ def main():
             "workload": shape.name,
             "tokens": shape.T, "hidden": shape.H, "expert_inter": shape.I, "experts": shape.E, "top_k": shape.k,
             "routing": shape.routing, "weight_layout": "k_major" if shape.kmajor else "row_major",
-            "weight_format": args.format,
+            "weight_format": args.format, "gate_up_twin": args.gate_up if shape.kmajor else "row_major",
             "weight_copies_cycled": L, "routing_batches_cycled": R,
             "launch": "eager" if args.eager else "hip_graph",
         },

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 2
+#define MOE_NVFP4_ABI_VERSION 3
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
 #define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
@@ -161,6 +161,31 @@ int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, i
                            float *h, void *stream);
 
 /*
+ * moe_nvfp4_gate_up_silu_concat — moe_nvfp4_gate_up_silu over a
+ * concatenated gate||up K-major twin (transpose.rs,
+ * transpose_concat_for_gemm_padded: gate and up, which share K = H, are
+ * transposed side by side into one twin with a padded row pitch, so one GEMM
+ * reads both; the result carries the first part's scale_2, and the caller
+ * ensures both parts share it).  Computes exactly what
+ * moe_nvfp4_gate_up_silu computes with
+ *     Wg_e = columns [0, I) and Wu_e = columns [I, 2I) of the twin.
+ *
+ *   gate_up   one table: packed[e] [K/2, pitch] and scale[e] [K/g, pitch]
+ *             (g = 16, or 32 for K_MAJOR_MXFP4) with rows `pitch` bytes
+ *             apart; columns 2I .. pitch are padding (never read);
+ *             scale2[e] serves both halves.  Layout K_MAJOR or
+ *             K_MAJOR_MXFP4.
+ *   pitch     row pitch of the twin in bytes: pitch >= 2I, pitch % 16 == 0.
+ * Other arguments, admission and errors as moe_nvfp4_gate_up_silu; ESHAPE
+ * also for a bad pitch, ELAYOUT for a row-major table.
+ */
+int moe_nvfp4_gate_up_silu_concat(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
+                                  int32_t I, moe_nvfp4_experts gate_up, int32_t pitch,
+                                  const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                                  const int32_t *active_experts, const int32_t *active_count,
+                                  float *h, void *stream);
+
+/*
  * moe_nvfp4_down — down projection over the SiLU product
  * (nvfp4_moe_grouped.rs, doc of moe_expert_down_act_nvfp4_grouped: k is the
  * intermediate width, rows of the activation and output are sorted
@@ -206,6 +231,20 @@ int moe_nvfp4_blend(const float *y, const float *topk_weights, const int32_t *pa
  * exceeds 2^40 bytes.
  */
 int transpose_u8(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, void *stream);
+
+/*
+ * transpose_u8_pitched — transpose_u8 into a column window of a wider matrix
+ * (transpose.rs, transpose_concat_for_gemm_padded and the shared
+ * implementation behind the concatenating builders, whose host loop writes
+ * part p at column offset n_off of rows `stride` bytes apart):
+ *     dst[c * dst_pitch + r] = src[r * cols + c]   for r < rows, c < cols.
+ * Bytes of dst outside those positions are not touched, so the caller zeroes
+ * pad columns and places each part by offsetting dst.
+ * Errors: ENULL; ESHAPE if rows < 1, cols < 1 or dst_pitch < rows; ELIMIT if
+ * rows * cols or dst_pitch * cols exceeds 2^40 bytes.
+ */
+int transpose_u8_pitched(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols,
+                         int64_t dst_pitch, void *stream);
 
 /*
  * moe_nvfp4_route — router ahead of the path: softmax over each token's

@@ -37,7 +37,10 @@ __all__ = [
     "moe_nvfp4_down",
     "moe_nvfp4_blend",
     "transpose_u8",
+    "transpose_u8_pitched",
     "transpose_for_gemm",
+    "transpose_concat_for_gemm",
+    "moe_nvfp4_gate_up_silu_concat",
     "moe_nvfp4_route",
     "with_shared_expert",
 ]
@@ -90,8 +93,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_blend.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
         L.transpose_u8.argtypes = [_P, _P, _I, _I, _P]
         L.moe_nvfp4_route.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+        L.transpose_u8_pitched.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P]
+        L.moe_nvfp4_gate_up_silu_concat.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _I, _P, _P, _P, _P, _P, _P]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
-                   "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version"):
+                   "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version", "transpose_u8_pitched",
+                   "moe_nvfp4_gate_up_silu_concat"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -159,7 +165,7 @@ class ExpertTables:
 
 
 # --------------------------------------------------------------------------
-# The five C entry points (argument marshalling only)
+# The C entry points (argument marshalling only)
 # --------------------------------------------------------------------------
 def moe_nvfp4_sort(topk_ids, E, expert_offsets, sorted_token_ids, pair_pos, active_experts,
                    active_count, err_flag, stream=None) -> None:
@@ -187,6 +193,22 @@ def moe_nvfp4_gate_up_silu(x, k, E, H, I, gate: ExpertTables, up: ExpertTables, 
         _dev(active_count, torch.int32, "active_count"),
         _dev(h, torch.float32, "h"), _stream(stream))
     _check("moe_nvfp4_gate_up_silu", rc)
+
+
+def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, expert_offsets,
+                                  sorted_token_ids, active_experts, active_count, h, stream=None) -> None:
+    """Gate+up over a concatenated gate||up K-major twin (rows ``pitch``
+    bytes apart, up columns from I on); see the C header."""
+    T = x.shape[0]
+    rc = lib().moe_nvfp4_gate_up_silu_concat(
+        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
+        T, k, E, H, I, gate_up.abi(), int(pitch),
+        _dev(expert_offsets, torch.int32, "expert_offsets"),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _dev(active_experts, torch.int32, "active_experts"),
+        _dev(active_count, torch.int32, "active_count"),
+        _dev(h, torch.float32, "h"), _stream(stream))
+    _check("moe_nvfp4_gate_up_silu_concat", rc)
 
 
 def moe_nvfp4_down(h, T, k, E, H, I, down: ExpertTables, expert_offsets, active_experts, active_count,
@@ -217,6 +239,18 @@ def transpose_u8(src, dst, rows, cols, stream=None) -> None:
     rc = lib().transpose_u8(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst"), rows, cols,
                             _stream(stream))
     _check("transpose_u8", rc)
+
+
+def transpose_u8_pitched(src, dst, rows, cols, dst_pitch, dst_offset=0, stream=None) -> None:
+    """dst.flat[dst_offset + c * dst_pitch + r] = src[r, c] (the C call on
+    dst's storage from byte dst_offset on)."""
+    if src.numel() != rows * cols:
+        raise ValueError("transpose_u8_pitched: src size does not match rows * cols")
+    if dst_offset < 0 or dst_pitch < rows or dst.numel() < dst_offset + (cols - 1) * dst_pitch + rows:
+        raise ValueError("transpose_u8_pitched: dst too small for the pitched window")
+    rc = lib().transpose_u8_pitched(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst") + dst_offset,
+                                    rows, cols, dst_pitch, _stream(stream))
+    _check("transpose_u8_pitched", rc)
 
 
 def moe_nvfp4_route(logits, k, topk_ids, topk_weights, stream=None) -> None:
@@ -263,6 +297,29 @@ def transpose_for_gemm(packed: torch.Tensor, scale: torch.Tensor, n: int, k: int
     return pt, st
 
 
+def transpose_concat_for_gemm(parts, k: int, group_size: int = 16, align: int = 16):
+    """Load-time concatenated K-major twin (transpose.rs,
+    transpose_concat_for_gemm_padded): parts [(packed [n, K/2], scale
+    [n, K/group], n), ...] sharing K, transposed side by side into packed
+    [K/2, stride] and scales [K/group, stride], stride = sum(n) rounded up to
+    ``align``, pad columns zero.  Returns (packed, scale, stride); the stream
+    is synchronized before returning."""
+    if not parts:
+        raise ValueError("transpose_concat_for_gemm: empty parts")
+    n_total = sum(n for _, _, n in parts)
+    stride = -(-n_total // align) * align
+    dev = parts[0][0].device
+    pt = torch.zeros((k // 2, stride), dtype=torch.uint8, device=dev)
+    st = torch.zeros((k // group_size, stride), dtype=torch.uint8, device=dev)
+    off = 0
+    for packed, scale, n in parts:
+        transpose_u8_pitched(packed, pt, n, k // 2, stride, off)
+        transpose_u8_pitched(scale, st, n, k // group_size, stride, off)
+        off += n
+    torch.cuda.current_stream().synchronize()
+    return pt, st, stride
+
+
 class MoeLayer:
     """Device buffers and the four calls of one MoE layer forward.
 
@@ -273,9 +330,11 @@ class MoeLayer:
     """
 
     def __init__(self, T: int, k: int, E: int, H: int, I: int, gate: ExpertTables, up: ExpertTables,
-                 down: ExpertTables, device="cuda"):
+                 down: ExpertTables, device="cuda", gate_up: Optional[ExpertTables] = None, pitch: int = 0):
         self.T, self.k, self.E, self.H, self.I = T, k, E, H, I
         self.gate, self.up, self.down = gate, up, down
+        # Optional concatenated gate||up twin (used instead of gate and up).
+        self.gate_up, self.pitch = gate_up, pitch
         P = T * k
         i32 = dict(dtype=torch.int32, device=device)
         self.expert_offsets = torch.empty(E + 1, **i32)
@@ -292,8 +351,13 @@ class MoeLayer:
         s = _stream(stream)
         moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
                        self.active_experts, self.active_count, self.err_flag, s)
-        moe_nvfp4_gate_up_silu(x, self.k, self.E, self.H, self.I, self.gate, self.up, self.expert_offsets,
-                               self.sorted_token_ids, self.active_experts, self.active_count, self.h, s)
+        if self.gate_up is not None:
+            moe_nvfp4_gate_up_silu_concat(x, self.k, self.E, self.H, self.I, self.gate_up, self.pitch,
+                                          self.expert_offsets, self.sorted_token_ids, self.active_experts,
+                                          self.active_count, self.h, s)
+        else:
+            moe_nvfp4_gate_up_silu(x, self.k, self.E, self.H, self.I, self.gate, self.up, self.expert_offsets,
+                                   self.sorted_token_ids, self.active_experts, self.active_count, self.h, s)
         moe_nvfp4_down(self.h, self.T, self.k, self.E, self.H, self.I, self.down, self.expert_offsets,
                        self.active_experts, self.active_count, self.y, s)
         moe_nvfp4_blend(self.y, topk_weights, self.pair_pos, self.out, s)

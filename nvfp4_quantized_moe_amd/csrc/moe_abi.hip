@@ -13,7 +13,7 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
 int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *sorted_tok,
                            const int32_t *offsets, const int32_t *active, const int32_t *nactive,
                            const moe_nvfp4_experts &A, const moe_nvfp4_experts *B, float *out, int N, int K,
-                           int P, int E, hipStream_t stream);
+                           int P, int E, int ldb, int up_off, hipStream_t stream);
 
 namespace {
 
@@ -47,8 +47,26 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
                                      gate, &up, h, I, H, T, P, E, (hipStream_t)stream);
     if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(true, gate.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
-                                  expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E,
+                                  expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E, I, 0,
                                   (hipStream_t)stream);
+}
+
+extern "C" int moe_nvfp4_gate_up_silu_concat(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
+                                             int32_t I, moe_nvfp4_experts gate_up, int32_t pitch,
+                                             const int32_t *expert_offsets, const int32_t *sorted_token_ids,
+                                             const int32_t *active_experts, const int32_t *active_count,
+                                             float *h, void *stream) {
+    if (!x || !expert_offsets || !sorted_token_ids || !active_experts || !active_count || !h)
+        return MOE_NVFP4_ENULL;
+    if (moe_host::experts_null(gate_up)) return MOE_NVFP4_ENULL;
+    const int rc = check_common(T, k, E, H, I, gate_up.layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    if (gate_up.layout == MOE_NVFP4_ROW_MAJOR) return MOE_NVFP4_ELAYOUT;
+    if ((int64_t)pitch < 2 * (int64_t)I || pitch % 16 != 0) return MOE_NVFP4_ESHAPE;
+    if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
+    return moe_launch_gemm_kmajor(true, gate_up.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
+                                  expert_offsets, active_experts, active_count, gate_up, nullptr, h, I, H,
+                                  T * k, E, pitch, I, (hipStream_t)stream);
 }
 
 extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
@@ -65,6 +83,6 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
                                      nullptr, y, H, I, T, P, E, (hipStream_t)stream);
     if ((uint64_t)P * I * 4 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(false, down.layout == MOE_NVFP4_K_MAJOR_MXFP4, h, nullptr, expert_offsets,
-                                  active_experts, active_count, down, nullptr, y, H, I, P, E,
+                                  active_experts, active_count, down, nullptr, y, H, I, P, E, H, 0,
                                   (hipStream_t)stream);
 }

@@ -72,6 +72,8 @@ struct GemmArgs {
     float *out;
     int N, K;
     int n_ct;      // column tiles
+    int ldb;       // row pitch of the K-major twins (packed and scale rows), bytes
+    int up_off;    // > 0: concatenated gate||up twin, up columns at this byte offset
 };
 
 // ---------------------------------------------------------------------------
@@ -309,15 +311,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool wact = n_w < N;
     const size_t row0 = (size_t)un.lo + un.m0;
 
+    // Separate gate and up tables, or one concatenated twin whose up columns
+    // start up_off bytes into each packed and scale row.
     const uint8_t *pA = a.pa[e];
-    const uint8_t *pB = a.pb[e];
+    const uint8_t *pB = a.up_off ? (pA ? pA + a.up_off : nullptr) : a.pb[e];
     if (pA == nullptr || pB == nullptr) {
         zero_rows(a, row0, mrows, n0, 128);
         return;
     }
     const bool up_wave = wave >= 2;
     const uint8_t *pk = up_wave ? pB : pA;
-    const uint8_t *sk = up_wave ? a.sb[e] : a.sa[e];
+    const uint8_t *sk = up_wave ? (a.up_off ? a.sa[e] + a.up_off : a.sb[e]) : a.sa[e];
+    const int ldb = a.ldb;
     const int n_ld = wact ? n_w : N - 64;  // idle waves (N not a multiple of 128) read valid columns
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
@@ -358,14 +363,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // scale row (l >> 4) & 1 (NVFP4: two groups of 16 k; MXFP4: its one
     // group of 32 k, loaded twice), columns 4 (l & 15) .. +3.
     const int bt = lane >> 2;
-    const uint32_t bdoff = (uint32_t)(4 * (bt & 3) + (bt >> 2)) * N + n_ld + 16 * (lane & 3);
+    const uint32_t bdoff = (uint32_t)(4 * (bt & 3) + (bt >> 2)) * ldb + n_ld + 16 * (lane & 3);
     constexpr int kSRows = MX ? 1 : 2;  // scale rows per 32-k step
-    const uint32_t sdoff = (uint32_t)(MX ? 0 : (lane >> 4) & 1) * N + n_ld + 4 * (lane & 15);
+    const uint32_t sdoff = (uint32_t)(MX ? 0 : (lane >> 4) & 1) * ldb + n_ld + 4 * (lane & 15);
     auto dma_b = [&](int s, auto st) {
         const int sc_ = s < S ? s : S - 1;
-        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(pk + (size_t)(16 * sc_) * N + bdoff),
+        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(pk + (size_t)(16 * sc_) * ldb + bdoff),
                                          (MOE_LDS void *)(wbuf(st) + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(sk + (size_t)(kSRows * sc_) * N + sdoff),
+        __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)(sk + (size_t)(kSRows * sc_) * ldb + sdoff),
                                          (MOE_LDS void *)(wbuf(st) + 4096 + wave * 256), 4, 0, 0);
     };
     const int brd = wave * 1024 + 64 * q + 4 * c, srd = 4096 + wave * 256 + 4 * (16 * (q >> 1) + c);
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j].
     // Up waves hand u = s2u * acc to the gate waves through LDS.
-    const float s2g = a.s2a[e], s2u = a.s2b[e];
+    const float s2g = a.s2a[e], s2u = a.up_off ? s2g : a.s2b[e];
     float *ex = reinterpret_cast<float *>(sa0);
     const int exc = 64 * (wave & 1) + 4 * c;  // column within the block's 128
     constexpr int kExTiles = kExRows / 16;
@@ -527,10 +532,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint8_t *sk = a.sa[e];
     const int n_ld = wact ? n_w : N - 64;
     // Per-lane byte offsets (32-bit) from wave-uniform bases.
-    const uint32_t boff = (uint32_t)(4 * q) * N + n_ld + 4 * c;
+    const int ldb = a.ldb;
+    const uint32_t boff = (uint32_t)(4 * q) * ldb + n_ld + 4 * c;
     // Scale row of k-octet q within a 32-k step: NVFP4 has two (groups of 16), MXFP4 one.
     constexpr int kSRows = MX ? 1 : 2;
-    const uint32_t soff = (uint32_t)(MX ? 0 : q >> 1) * N + n_ld + 4 * c;
+    const uint32_t soff = (uint32_t)(MX ? 0 : q >> 1) * ldb + n_ld + 4 * c;
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
 
@@ -566,10 +572,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     uint32_t bs[kBDist];
     auto load_b = [&](int slot_s, uint32_t (&w)[4], uint32_t &sv) {
         const int s = slot_s < S ? slot_s : S - 1;
-        const uint8_t *p = pk + (size_t)(16 * s) * N;
+        const uint8_t *p = pk + (size_t)(16 * s) * ldb;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = gload<uint32_t>(p + (size_t)r * N + boff);
-        sv = gload<uint32_t>(sk + (size_t)(kSRows * s) * N + soff);
+        for (int r = 0; r < 4; ++r) w[r] = gload<uint32_t>(p + (size_t)r * ldb + boff);
+        sv = gload<uint32_t>(sk + (size_t)(kSRows * s) * ldb + soff);
     };
 
     f32x4_t acc[kMTD][4];
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *sorted_tok,
                            const int32_t *offsets, const int32_t *active, const int32_t *nactive,
                            const moe_nvfp4_experts &A, const moe_nvfp4_experts *B, float *out, int N, int K,
-                           int P, int E, hipStream_t stream) {
+                           int P, int E, int ldb, int up_off, hipStream_t stream) {
     GemmArgs a;
     a.act = act;
     a.sorted_tok = sorted_tok;
@@ -682,6 +688,8 @@ int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *
     a.out = out;
     a.N = N;
     a.K = K;
+    a.ldb = ldb;
+    a.up_off = up_off;
     const int cols = gated ? 128 : 256;
     a.n_ct = (N + cols - 1) / cols;
     // Row tiles: sum over experts of ceil(rows / R) <= ceil(P / R) + min(E, P).

@@ -1,8 +1,11 @@
-// Byte-matrix transpose dst[c * rows + r] = src[r * cols + c].
+// Byte-matrix transpose dst[c * pitch + r] = src[r * cols + c] (pitch = rows
+// for the plain transpose).
 //
 // transpose.rs, transpose_for_gemm_gs: the load-time twin of an NVFP4 weight
 // is the byte transpose of its packed [N, K/2] and scale [N, K/16] tensors
-// (nibble pairs stay together).  HBM-bound copy: a 64x64-byte tile moves
+// (nibble pairs stay together); transpose_concat_for_gemm_padded writes
+// several such transposes side by side into one twin whose rows are `pitch`
+// bytes apart.  HBM-bound copy: a 64x64-byte tile moves
 // through LDS so both the read of src rows and the write of dst rows are
 // 16-byte coalesced; ragged or unaligned edges fall back to byte accesses.
 #include "moe_common.hpp"
@@ -15,7 +18,7 @@ constexpr int kTransposeThreads = 256;
 
 __global__ __launch_bounds__(kTransposeThreads) void k_transpose_u8(const uint8_t *__restrict__ src,
                                                                    uint8_t *__restrict__ dst, int rows,
-                                                                   int cols, int tiles_c) {
+                                                                   int cols, int tiles_c, int64_t pitch) {
     __shared__ uint32_t tile_w[kTile * kTileStride / 4];
     uint8_t *tile = reinterpret_cast<uint8_t *>(tile_w);
 
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(kTransposeThreads) void k_transpose_u8(const uint8_
                 for (int b = 0; b < 4; ++b) v |= (uint32_t)tile[(seg + q * 4 + b) * kTileStride + a] << (8 * b);
                 wv[q] = v;
             }
-            uint8_t *d = dst + (size_t)c * rows + r;
+            uint8_t *d = dst + (size_t)c * (size_t)pitch + r;
             if (r + 16 <= rows && ((reinterpret_cast<uintptr_t>(d) & 15) == 0)) {
                 *reinterpret_cast<uint4 *>(d) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             } else {
@@ -66,15 +69,24 @@ __global__ __launch_bounds__(kTransposeThreads) void k_transpose_u8(const uint8_
     }
 }
 
-}  // namespace
-
-extern "C" int transpose_u8(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, void *stream) {
+int launch_transpose(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, int64_t pitch, void *stream) {
     if (!src || !dst) return MOE_NVFP4_ENULL;
-    if (rows < 1 || cols < 1) return MOE_NVFP4_ESHAPE;
-    if ((int64_t)rows * cols > (int64_t(1) << 40)) return MOE_NVFP4_ELIMIT;
+    if (rows < 1 || cols < 1 || pitch < rows) return MOE_NVFP4_ESHAPE;
+    if ((int64_t)rows * cols > (int64_t(1) << 40) || pitch * cols > (int64_t(1) << 40)) return MOE_NVFP4_ELIMIT;
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     if (tiles_r * tiles_c > 0x7fffffffLL) return MOE_NVFP4_ELIMIT;
     hipLaunchKernelGGL(k_transpose_u8, dim3((unsigned)(tiles_r * tiles_c)), dim3(kTransposeThreads), 0,
-                       (hipStream_t)stream, src, dst, rows, cols, (int)tiles_c);
+                       (hipStream_t)stream, src, dst, rows, cols, (int)tiles_c, pitch);
     return moe_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" int transpose_u8(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols, void *stream) {
+    return launch_transpose(src, dst, rows, cols, rows, stream);
+}
+
+extern "C" int transpose_u8_pitched(const uint8_t *src, uint8_t *dst, int32_t rows, int32_t cols,
+                                    int64_t dst_pitch, void *stream) {
+    return launch_transpose(src, dst, rows, cols, dst_pitch, stream);
 }

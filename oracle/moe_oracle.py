@@ -142,6 +142,24 @@ def transpose_u8(src: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(src.T)
 
 
+def transpose_concat(parts, stride: int) -> np.ndarray:
+    """Concatenated transposed twin (transpose.rs page, doc of
+    ``transpose_concat_for_gemm_padded`` and the implementation behind the
+    concatenating builders): byte matrices [n_p, cols] sharing cols are
+    transposed side by side, part p at columns [off_p, off_p + n_p) of a
+    [cols, stride] matrix, off_p the sum of the earlier n; the pad columns
+    sum(n) .. stride are zero."""
+    cols = parts[0].shape[1]
+    out = np.zeros((cols, stride), dtype=np.uint8)
+    off = 0
+    for p in parts:
+        assert p.dtype == np.uint8 and p.shape[1] == cols
+        out[:, off: off + p.shape[0]] = p.T
+        off += p.shape[0]
+    assert off <= stride
+    return out
+
+
 # --------------------------------------------------------------------------
 # Router (ahead of the path: softmax over the expert logits, top k kept,
 # weights renormalised over them).  The pages show only the router's logit

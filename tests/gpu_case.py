@@ -25,7 +25,7 @@ def say(*a):
 class Case:
     def __init__(self, cfg_id: int, shape: synth.MoeShape | None = None, nulls=(), kmajor: bool | None = None,
                  ids: np.ndarray | None = None, weights: np.ndarray | None = None, all_experts: bool = False,
-                 fmt: str = "nvfp4", gen=None):
+                 fmt: str = "nvfp4", gen=None, concat: bool = False):
         self.cfg_id = cfg_id
         self.shape = shape or synth.config(cfg_id)
         s = self.shape
@@ -62,7 +62,27 @@ class Case:
         self.x = torch.from_numpy(self.x_bits.view(np.int16)).cuda().view(torch.bfloat16)
         self.ids_d = torch.from_numpy(self.ids).cuda()
         self.w_d = torch.from_numpy(self.w).cuda()
-        self.layer = moe.MoeLayer(s.T, s.k, s.E, s.H, s.I, *self.tables)
+        # Optional concatenated gate||up twin per expert (K-major only), built
+        # from the row-major bytes with the pitched transpose.
+        self.concat = concat
+        self.pitch = 0
+        gate_up = None
+        if concat:
+            assert self.kmajor
+            rows = []
+            for e in range(s.E):
+                if (e, 0) not in self.dev:
+                    rows.append(None)
+                    continue
+                parts = []
+                for proj in (0, 1):
+                    pk, sc = self.gen(cfg_id, e, proj, s)
+                    parts.append((torch.from_numpy(pk).cuda(), torch.from_numpy(sc).cuda(), s.I))
+                pt, st, self.pitch = moe.transpose_concat_for_gemm(parts, s.H, group, align=16)
+                self.dev[(e, "gate_up")] = (pt, st)
+                rows.append((pt, st, self.scale2[0]))
+            gate_up = moe.ExpertTables(rows, self.layout)
+        self.layer = moe.MoeLayer(s.T, s.k, s.E, s.H, s.I, *self.tables, gate_up=gate_up, pitch=self.pitch)
 
     def _table(self, proj, layout):
         rows = []

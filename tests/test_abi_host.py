@@ -16,10 +16,11 @@ def test_library_exports_every_header_function():
     L = moe.lib()
     names = moe.header_functions()
     assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
-                          "transpose_u8", "moe_nvfp4_abi_version"}
+                          "transpose_u8", "moe_nvfp4_abi_version", "moe_nvfp4_route", "transpose_u8_pitched",
+                          "moe_nvfp4_gate_up_silu_concat"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 2
+    assert L.moe_nvfp4_abi_version() == 3
 
 
 def _ex(layout=0, null=False):
@@ -100,3 +101,23 @@ def test_route_rejects():
     assert L.moe_nvfp4_route(D, 4, 2000, 2, D, D, None) == ELIMIT  # E > MOE_NVFP4_MAX_EXPERTS
     assert L.moe_nvfp4_route(D, 4, 128, 65, D, D, None) == ELIMIT  # k > 64
     assert L.moe_nvfp4_route(D, 1 << 20, 8, 8, D, D, None) == ELIMIT  # T * k > MOE_NVFP4_MAX_PAIRS
+
+
+def test_concat_gate_up_and_pitched_transpose_reject():
+    L = moe.lib()
+
+    def call(x=D, T=4, k=2, E=4, H=256, I=512, gu=None, pitch=1024, h=D):
+        return L.moe_nvfp4_gate_up_silu_concat(x, T, k, E, H, I, gu or _ex(1), pitch, D, D, D, D, h, None)
+
+    assert call(x=None) == ENULL
+    assert call(gu=_ex(1, null=True)) == ENULL
+    assert call(gu=_ex(0)) == ELAYOUT                   # the concatenated twin is K-major
+    assert call(gu=_ex(5)) == ELAYOUT
+    assert call(pitch=1008) == ESHAPE                   # pitch < 2I
+    assert call(pitch=1032) == ESHAPE                   # pitch % 16 != 0
+    assert call(H=96) == ESHAPE
+    assert call(T=1 << 16, H=1 << 15) == ELIMIT         # x of 4 GiB or more
+    assert L.transpose_u8_pitched(None, D, 4, 4, 4, None) == ENULL
+    assert L.transpose_u8_pitched(D, D, 4, 4, 3, None) == ESHAPE    # pitch < rows
+    assert L.transpose_u8_pitched(D, D, 0, 4, 4, None) == ESHAPE
+    assert L.transpose_u8_pitched(D, D, 4, 1 << 30, 1 << 12, None) == ELIMIT

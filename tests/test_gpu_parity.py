@@ -430,3 +430,53 @@ def test_mxfp4_null_expert_and_scale_range():
             rel = np.abs(g - w) / (col + np.abs(w) + 1e-300)
             assert rel.max() <= 1e-2, (name, int(e), float(rel.max()))
     say("mx range ok", float(np.abs(ref["h"][:n]).max()), float(np.abs(ref["h"][:n][ref["h"][:n] != 0]).min()))
+
+
+# ---------------------------------------------------------------- concatenated gate||up twin (next step F4)
+@pytest.mark.parametrize("rows,cols,parts", [(1536, 2048, 2), (70, 130, 2), (64, 96, 3)])
+def test_transpose_concat_bit_exact(rows, cols, parts):
+    say("transpose concat", rows, cols, parts)
+    rng = np.random.default_rng(rows + cols)
+    srcs = [rng.integers(0, 256, (rows + 3 * p, cols), dtype=np.uint8) for p in range(parts)]
+    n_total = sum(a.shape[0] for a in srcs)
+    stride = -(-n_total // 16) * 16
+    dst = torch.full((cols, stride), 0x5A, dtype=torch.uint8, device="cuda")
+    off = 0
+    for a in srcs:
+        moe.transpose_u8_pitched(torch.from_numpy(a).cuda(), dst, a.shape[0], cols, stride, off)
+        off += a.shape[0]
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    want = oracle.transpose_concat(srcs, stride)
+    assert np.array_equal(got[:, :n_total], want[:, :n_total])
+    assert (got[:, n_total:] == 0x5A).all()  # bytes outside the windows untouched
+    # the Python builder zeroes the pad columns
+    pt, st, stride2 = moe.transpose_concat_for_gemm(
+        [(torch.from_numpy(a).cuda(), torch.from_numpy(a[:, : cols // 8].copy()).cuda(), a.shape[0]) for a in srcs],
+        2 * cols, 16, align=16)
+    assert stride2 == stride and np.array_equal(pt.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_layer_prefill_concat_gate_up_full(fmt):
+    """The many-token workload with each expert's gate and up in one
+    concatenated K-major twin; h must equal the two-twin launch bit for bit
+    (same arithmetic, other addressing) and the oracle to the parity rules."""
+    say("layer cfg 5, concatenated gate||up", fmt)
+    case = Case(5, fmt=fmt, concat=True)
+    _full_check(case, f"cfg5 concat {fmt}")
+    h_concat = case.layer.h.clone()
+    L = case.layer
+    moe.moe_nvfp4_gate_up_silu(case.x, case.shape.k, case.shape.E, case.shape.H, case.shape.I, L.gate, L.up,
+                               L.expert_offsets, L.sorted_token_ids, L.active_experts, L.active_count, L.h)
+    torch.cuda.synchronize()
+    n = int(L.expert_offsets[-1].item())
+    assert torch.equal(h_concat[:n], L.h[:n])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 1216, 704, 5, 3), (130, 256, 320, 4, 2)])
+def test_ragged_concat_gate_up(T, H, I, E, k, fmt):
+    say("ragged concat", T, H, I, E, k, fmt)
+    shape = synth.MoeShape(f"ragged_cc_{T}_{H}_{I}_{E}_{k}", T, H, I, E, k, "uniform", True)
+    _full_check(Case(23, shape, fmt=fmt, concat=True, nulls=(1,)), f"ragged concat {T},{H},{I},{E},{k},{fmt}")

@@ -213,6 +213,38 @@ def test_mx_group_of_16_is_caught():
     assert not np.array_equal(wrong, ref)
 
 
+# ---------------------------------------------------------------- concatenated gate||up twin
+def test_transpose_concat_bruteforce_and_windows():
+    """Index formula of the pages' host loop, written out as scalar loops:
+    part p's byte (i, j) lands at row j, column off_p + i of rows `stride`
+    apart; pad columns stay zero; each column window dequantises to its part."""
+    rng = np.random.default_rng(3)
+    n_a, n_b, cols, stride = 5, 7, 6, 16
+    a = rng.integers(0, 256, (n_a, cols), dtype=np.uint8)
+    b = rng.integers(0, 256, (n_b, cols), dtype=np.uint8)
+    got = oracle.transpose_concat([a, b], stride)
+    flat = [0] * (cols * stride)
+    off = 0
+    for part in (a, b):
+        for i in range(part.shape[0]):
+            for j in range(cols):
+                flat[j * stride + off + i] = int(part[i, j])
+        off += part.shape[0]
+    assert got.reshape(-1).tolist() == flat
+    assert not got[:, n_a + n_b:].any()
+    # gate and up of one expert: the windows of the twin are their own twins
+    shape = synth.MoeShape("t", 1, 128, 64, 1, 1, "uniform", True)
+    (gp, gs), (up, us) = synth.gen_expert(1, 0, 0, shape), synth.gen_expert(1, 0, 1, shape)
+    P = oracle.transpose_concat([gp, up], 144)
+    S = oracle.transpose_concat([gs, us], 144)
+    s2 = synth.SCALE2_F32
+    for (pk, sc), off in (((gp, gs), 0), ((up, us), 64)):
+        W = oracle.dequant(pk, sc, s2, 64, 128)
+        Wt = oracle.dequant(np.ascontiguousarray(P[:, off:off + 64]), np.ascontiguousarray(S[:, off:off + 64]),
+                            s2, 64, 128, kmajor=True)
+        assert np.array_equal(W, Wt)
+
+
 # ---------------------------------------------------------------- P4: transpose
 def test_transpose_bruteforce_and_involution():
     rng = np.random.default_rng(1)
