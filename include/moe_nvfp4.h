@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 3
+#define MOE_NVFP4_ABI_VERSION 4
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
 #define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
@@ -159,6 +159,25 @@ int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, int32_t E, i
                            const int32_t *expert_offsets, const int32_t *sorted_token_ids,
                            const int32_t *active_experts, const int32_t *active_count,
                            float *h, void *stream);
+
+/*
+ * moe_nvfp4_sort_gate_up_silu — moe_nvfp4_sort followed by
+ * moe_nvfp4_gate_up_silu (the first two steps of nvfp4_moe_grouped.rs,
+ * module doc), enqueued as ONE launch when the weights are ROW_MAJOR, the
+ * P = T*k pairs number at most 64 and every expert's rows fit one staging
+ * pass of the decode kernel (the few-token decode case, where a launch costs
+ * more than the sort's work); otherwise as the two launches.  Every output
+ * (the sort's five, err_flag, h) is defined exactly as by the two calls and
+ * is complete when the work enqueued on `stream` is; err_flag is zeroed by
+ * the caller as for moe_nvfp4_sort.  Arguments, admission and errors are the
+ * union of the two calls'.
+ */
+int moe_nvfp4_sort_gate_up_silu(const int32_t *topk_ids, const uint16_t *x, int32_t T, int32_t k,
+                                int32_t E, int32_t H, int32_t I, moe_nvfp4_experts gate,
+                                moe_nvfp4_experts up, int32_t *expert_offsets,
+                                int32_t *sorted_token_ids, int32_t *pair_pos,
+                                int32_t *active_experts, int32_t *active_count, uint32_t *err_flag,
+                                float *h, void *stream);
 
 /*
  * moe_nvfp4_gate_up_silu_concat — moe_nvfp4_gate_up_silu over a

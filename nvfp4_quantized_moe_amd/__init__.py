@@ -41,6 +41,7 @@ __all__ = [
     "transpose_for_gemm",
     "transpose_concat_for_gemm",
     "moe_nvfp4_gate_up_silu_concat",
+    "moe_nvfp4_sort_gate_up_silu",
     "moe_nvfp4_route",
     "with_shared_expert",
 ]
@@ -95,9 +96,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_route.argtypes = [_P, _I, _I, _I, _P, _P, _P]
         L.transpose_u8_pitched.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P]
         L.moe_nvfp4_gate_up_silu_concat.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _I, _P, _P, _P, _P, _P, _P]
+        L.moe_nvfp4_sort_gate_up_silu.argtypes = [_P, _P, _I, _I, _I, _I, _I, _Experts, _Experts, _P, _P, _P, _P,
+                                                  _P, _P, _P, _P]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                    "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version", "transpose_u8_pitched",
-                   "moe_nvfp4_gate_up_silu_concat"):
+                   "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -193,6 +196,25 @@ def moe_nvfp4_gate_up_silu(x, k, E, H, I, gate: ExpertTables, up: ExpertTables, 
         _dev(active_count, torch.int32, "active_count"),
         _dev(h, torch.float32, "h"), _stream(stream))
     _check("moe_nvfp4_gate_up_silu", rc)
+
+
+def moe_nvfp4_sort_gate_up_silu(topk_ids, x, E, H, I, gate: ExpertTables, up: ExpertTables, expert_offsets,
+                                sorted_token_ids, pair_pos, active_experts, active_count, err_flag, h,
+                                stream=None) -> None:
+    """Sort then gate+up (one launch in the few-token decode case); see the C header."""
+    T, k = topk_ids.shape
+    rc = lib().moe_nvfp4_sort_gate_up_silu(
+        _dev(topk_ids, torch.int32, "topk_ids"),
+        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
+        T, k, E, H, I, gate.abi(), up.abi(),
+        _dev(expert_offsets, torch.int32, "expert_offsets"),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
+        _dev(pair_pos, torch.int32, "pair_pos"),
+        _dev(active_experts, torch.int32, "active_experts"),
+        _dev(active_count, torch.int32, "active_count"),
+        _dev(err_flag, torch.int32, "err_flag"),
+        _dev(h, torch.float32, "h"), _stream(stream))
+    _check("moe_nvfp4_sort_gate_up_silu", rc)
 
 
 def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, expert_offsets,
@@ -347,15 +369,24 @@ class MoeLayer:
         self.y = torch.empty((P, H), dtype=torch.float32, device=device)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
 
-    def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, stream=None):
+    def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, stream=None,
+                fuse_sort: bool = True):
+        """``fuse_sort``: sort and gate+up through moe_nvfp4_sort_gate_up_silu
+        (one launch for few-token decode); False issues the two calls."""
         s = _stream(stream)
-        moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
-                       self.active_experts, self.active_count, self.err_flag, s)
         if self.gate_up is not None:
+            moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
+                           self.active_experts, self.active_count, self.err_flag, s)
             moe_nvfp4_gate_up_silu_concat(x, self.k, self.E, self.H, self.I, self.gate_up, self.pitch,
                                           self.expert_offsets, self.sorted_token_ids, self.active_experts,
                                           self.active_count, self.h, s)
+        elif fuse_sort:
+            moe_nvfp4_sort_gate_up_silu(topk_ids, x, self.E, self.H, self.I, self.gate, self.up,
+                                        self.expert_offsets, self.sorted_token_ids, self.pair_pos,
+                                        self.active_experts, self.active_count, self.err_flag, self.h, s)
         else:
+            moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
+                           self.active_experts, self.active_count, self.err_flag, s)
             moe_nvfp4_gate_up_silu(x, self.k, self.E, self.H, self.I, self.gate, self.up, self.expert_offsets,
                                    self.sorted_token_ids, self.active_experts, self.active_count, self.h, s)
         moe_nvfp4_down(self.h, self.T, self.k, self.E, self.H, self.I, self.down, self.expert_offsets,

@@ -9,7 +9,10 @@
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
-                          hipStream_t stream);
+                          hipStream_t stream, const MoeSortFuse *fuse);
+int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets, int32_t *sorted_tok,
+                    int32_t *pair_pos, int32_t *active, int32_t *active_count, uint32_t *err_flag,
+                    hipStream_t stream);
 int moe_launch_gemm_kmajor(bool gated, bool mx, const void *act, const int32_t *sorted_tok,
                            const int32_t *offsets, const int32_t *active, const int32_t *nactive,
                            const moe_nvfp4_experts &A, const moe_nvfp4_experts *B, float *out, int N, int K,
@@ -44,11 +47,39 @@ extern "C" int moe_nvfp4_gate_up_silu(const uint16_t *x, int32_t T, int32_t k, i
     const int P = T * k;
     if (gate.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count,
-                                     gate, &up, h, I, H, T, P, E, (hipStream_t)stream);
+                                     gate, &up, h, I, H, T, P, E, (hipStream_t)stream, nullptr);
     if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(true, gate.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
                                   expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E, I, 0,
                                   (hipStream_t)stream);
+}
+
+extern "C" int moe_nvfp4_sort_gate_up_silu(const int32_t *topk_ids, const uint16_t *x, int32_t T, int32_t k,
+                                           int32_t E, int32_t H, int32_t I, moe_nvfp4_experts gate,
+                                           moe_nvfp4_experts up, int32_t *expert_offsets,
+                                           int32_t *sorted_token_ids, int32_t *pair_pos, int32_t *active_experts,
+                                           int32_t *active_count, uint32_t *err_flag, float *h, void *stream) {
+    if (!topk_ids || !x || !expert_offsets || !sorted_token_ids || !pair_pos || !active_experts ||
+        !active_count || !err_flag || !h)
+        return MOE_NVFP4_ENULL;
+    if (moe_host::experts_null(gate) || moe_host::experts_null(up)) return MOE_NVFP4_ENULL;
+    if (gate.layout != up.layout) return MOE_NVFP4_ELAYOUT;
+    const int rc = check_common(T, k, E, H, I, gate.layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    const int P = T * k;
+    const hipStream_t st = (hipStream_t)stream;
+    if (gate.layout == MOE_NVFP4_ROW_MAJOR) {
+        const MoeSortFuse fuse{topk_ids, k, expert_offsets, sorted_token_ids, pair_pos, active_experts,
+                               active_count, err_flag};
+        return moe_launch_decode_row(true, x, sorted_token_ids, expert_offsets, active_experts, active_count, gate,
+                                     &up, h, I, H, T, P, E, st, &fuse);
+    }
+    if ((uint64_t)T * H * 2 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
+    const int src = moe_launch_sort(topk_ids, T, k, E, expert_offsets, sorted_token_ids, pair_pos, active_experts,
+                                    active_count, err_flag, st);
+    if (src != MOE_NVFP4_OK) return src;
+    return moe_launch_gemm_kmajor(true, gate.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
+                                  expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E, I, 0, st);
 }
 
 extern "C" int moe_nvfp4_gate_up_silu_concat(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,
@@ -80,7 +111,7 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
     const int P = T * k;
     if (down.layout == MOE_NVFP4_ROW_MAJOR)
         return moe_launch_decode_row(false, h, nullptr, expert_offsets, active_experts, active_count, down,
-                                     nullptr, y, H, I, T, P, E, (hipStream_t)stream);
+                                     nullptr, y, H, I, T, P, E, (hipStream_t)stream, nullptr);
     if ((uint64_t)P * I * 4 > 0xffffffffull) return MOE_NVFP4_ELIMIT;  // 32-bit activation offsets
     return moe_launch_gemm_kmajor(false, down.layout == MOE_NVFP4_K_MAJOR_MXFP4, h, nullptr, expert_offsets,
                                   active_experts, active_count, down, nullptr, y, H, I, P, E, H, 0,

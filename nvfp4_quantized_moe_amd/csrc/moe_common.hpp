@@ -128,6 +128,18 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return min(min(a, b), min(c, d));
 }
 
+// Mask of the lanes whose id equals this lane's (among lanes with valid set),
+// from one ballot per id bit.
+__device__ __forceinline__ unsigned long long match_lanes(int e, bool valid, int nbits) {
+    unsigned long long eq = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long m = __ballot(valid && bit);
+        eq &= bit ? m : ~m;
+    }
+    return eq;
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
     return z / (1.0f + __expf(-z));
 }
@@ -144,6 +156,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // ---------------------------------------------------------------------------
 // Host-side helpers.
 // ---------------------------------------------------------------------------
+// Routing-sort arguments handed to a gate+up launch that may run the sort
+// itself (moe_nvfp4_sort_gate_up_silu).
+struct MoeSortFuse {
+    const int32_t *topk_ids;
+    int k;
+    int32_t *offsets, *sorted_tok, *pair_pos, *active, *active_count;
+    uint32_t *err_flag;
+};
+
 namespace moe_host {
 
 inline bool experts_null(const moe_nvfp4_experts &w) {

@@ -65,7 +65,7 @@ constexpr int kSegBytes = 256;     // bytes of one weight row per step (512 k)
 constexpr int kMaxTG = 4;          // token groups of 4 per pass (16 rows)
 constexpr int kLdsBudget = 72 * 1024;  // staged activation rows per block (two blocks per CU)
 constexpr int kScaleLds = 1024;        // per wave: 4 steps x 8 rows x 32 bytes
-constexpr int kPreLds = 4 * (MOE_NVFP4_MAX_EXPERTS + 4);  // per-slot prefix sums of passes
+constexpr int kPreLds = 4 * (MOE_NVFP4_MAX_EXPERTS + 4);  // per-slot prefix sums of passes (or the fused sort)
 constexpr int kRmaxOff = kWaves * kScaleLds;                    // per-row maxima (16 x u32)
 constexpr int kPreOff = kRmaxOff + 64;
 constexpr int kHdrLds = kPreOff + kPreLds;  // scale areas + row maxima + pass prefix; then the rows
@@ -95,6 +95,24 @@ struct DecArgs {
     int ldx;                    // staged row stride, fp16 elements
     int extra;                  // block rows for passes beyond each expert's first
     int single_token;           // gate+up with T == 1: every routed row is token 0
+    // Routing sort fused into the gate+up launch (few pairs, one pass per
+    // expert): the routed ids, and the sort outputs that block (0, 0) writes.
+    int fused_sort;
+    int P, topk, E;
+    const int32_t *topk_ids;
+    int32_t *sort_offsets, *sort_tok, *sort_pos, *sort_active, *sort_count;
+    uint32_t *err_flag;
+};
+
+// The fused sort's tables, in the LDS area the pass prefix would otherwise
+// use: the token of every sorted position, and (for the block that writes
+// the sort outputs) the active experts in ascending order with, for each,
+// the number of routed pairs with a smaller id (its first sorted position).
+constexpr int kSortPairs = 64;
+struct SortLds {
+    int active[kSortPairs];
+    int lo[kSortPairs];
+    int tok[kSortPairs];
 };
 
 // 8 E2M1 codes (one 32-bit word: k .. k+7) times the block scale, as fp16.
@@ -307,7 +325,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
 
 // One pass: rows [row0, row0 + pr) of the expert against units
 // [u_first, u_first + nu) of its weights.
-template <bool GATED, int D>
+template <bool GATED, int D, bool TOK_LDS>  // TOK_LDS: pass tokens from the fused sort's LDS table
 __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                          const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
                                          const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
@@ -385,7 +403,12 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     // rest of the ring is in flight.
     const bool x_first = !GATED || a.single_token;
     int tokv = 0;  // gate+up: token of row (lane & 15) of the pass
-    if (!x_first) tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    if (!x_first) {
+        if constexpr (TOK_LDS)
+            tokv = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[row0 + min(lane & 15, pr - 1)];
+        else
+            tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    }
     __syncthreads();  // rmax cleared
     __builtin_amdgcn_sched_barrier(0);
     if (x_first) {
@@ -579,14 +602,12 @@ __device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
     return lo;
 }
 
-template <bool GATED>
-__device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, uint8_t *lds) {
-    const int e = a.active[slot];  // -1 past the active count
-    if (e < 0) return;
+// One pass of expert e, whose rows are the sorted positions [lo, hi).
+template <bool GATED, bool TOK_LDS>
+__device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, int hi, int pass, int u_first,
+                                             int nu, uint8_t *lds) {
     // Every table entry of expert e is read at once (e < E, so each read is
-    // in bounds): one round of dependent loads after the active list, not
-    // one per table.
-    const int lo = a.offsets[e], hi = a.offsets[e + 1];
+    // in bounds): one round of dependent loads, not one per table.
     const uint8_t *pA = a.pa[e];
     const uint8_t *pB = GATED ? a.pb[e] : pA;
     const uint8_t *sA = a.sa[e];
@@ -608,7 +629,78 @@ __device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, in
         }
         return;
     }
-    run_pass<GATED, kDepth>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+    run_pass<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+}
+
+template <bool GATED>
+__device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, uint8_t *lds) {
+    const int e = a.active[slot];  // -1 past the active count
+    if (e < 0) return;
+    do_pass_rows<GATED, false>(a, e, a.offsets[e], a.offsets[e + 1], pass, u_first, nu, lds);
+}
+
+// Routing sort of P <= 64 pairs inside the block (the sort step fused into
+// the gate+up launch when every expert's rows fit one pass).  Every wave
+// ranks the pairs itself, one per lane, so no wave waits for another: the
+// sorted position of a valid pair is the number of valid pairs with a
+// smaller id plus those with its id earlier in flat order (stable), and the
+// active experts are the first occurrences ranked by id.  Each wave writes
+// the same LDS tables (its own later reads then need no barrier).  Returns
+// (expert, first sorted position, rows) of active slot `slot`, expert -1
+// past the active count.  Block (0, 0) also writes every output of
+// moe_nvfp4_sort, the experts split over its waves.
+__device__ __forceinline__ int3 fused_sort(const DecArgs &a, SortLds *sl, int slot) {
+    const int lane = threadIdx.x & 63, w = moe::wave_id();
+    const int P = a.P, E = a.E;
+    const int id = lane < P ? a.topk_ids[lane] : -1;
+    const bool valid = lane < P && id >= 0 && id < E;
+    const unsigned long long vmask = __ballot(valid);
+    const unsigned long long same = moe::match_lanes(id, valid, E > 1 ? 32 - __clz(E - 1) : 0);
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const bool first = valid && (same & lt) == 0ull;
+    const unsigned long long fmask = __ballot(first);
+    int less = 0, dless = 0;  // valid pairs / distinct ids below this lane's id
+    for (int i = 0; i < P; ++i) {
+        const int v = __builtin_amdgcn_readlane(id, i);
+        less += ((vmask >> i) & 1ull) && v < id ? 1 : 0;
+        dless += ((fmask >> i) & 1ull) && v < id ? 1 : 0;
+    }
+    const int rows = __popcll(same);
+    const int pos = valid ? less + __popcll(same & lt) : -1;
+    if (valid) sl->tok[pos] = lane / a.topk;
+    const unsigned long long hit = __ballot(first && dless == slot);
+    int3 r = make_int3(-1, 0, 0);
+    if (hit != 0ull) {
+        const int L = __ffsll((long long)hit) - 1;
+        r = make_int3(__builtin_amdgcn_readlane(id, L), __builtin_amdgcn_readlane(less, L),
+                      __builtin_amdgcn_readlane(rows, L));
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+        if (first) {
+            sl->active[dless] = id;
+            sl->lo[dless] = less;
+        }
+        const int count = __popcll(fmask), total = __popcll(vmask);
+        if (w == 0) {
+            if (lane < P) a.sort_pos[lane] = pos;
+            if (lane == 0 && total < P) atomicOr(a.err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
+            if (lane == 0) *a.sort_count = count;
+        }
+        for (int e = moe::kWave * w + lane; e <= E; e += kThreads) {
+            // offsets[e]: valid pairs below e = first position of the first
+            // active expert at or above e (binary search), else all of them.
+            int lo = 0, hi = count;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (sl->active[mid] < e) lo = mid + 1;
+                else hi = mid;
+            }
+            a.sort_offsets[e] = lo < count ? sl->lo[lo] : total;
+            if (e < E) a.sort_active[e] = e < count ? sl->active[e] : -1;
+        }
+        for (int p = moe::kWave * w + lane; p < P; p += kThreads) a.sort_tok[p] = p < total ? sl->tok[p] : -1;
+    }
+    return r;
 }
 
 // Block (x, y): units [x G, x G + G) of
@@ -624,6 +716,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     const int nu = min(a.G, a.units - u_first);
     if (nu <= 0) return;
     const int y = blockIdx.y;
+    if (GATED && a.fused_sort) {  // extra == 0: one pass per expert
+        const int3 r = fused_sort(a, reinterpret_cast<SortLds *>(lds + kPreOff), y);
+        if (r.x < 0) return;  // past the active count
+        do_pass_rows<GATED, true>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, lds);
+        return;
+    }
     if (y >= a.extra) {
         do_pass<GATED>(a, y - a.extra, 0, u_first, nu, lds);
         return;
@@ -767,11 +865,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
 
 // Launch the row-major grouped projection (used by the two C-ABI entry points).
 // Shapes: N % 64 == 0, K % 64 == 0 and K >= 256 (checked by the callers).
+int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets, int32_t *sorted_tok,
+                    int32_t *pair_pos, int32_t *active, int32_t *active_count, uint32_t *err_flag,
+                    hipStream_t stream);
+
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
-                          hipStream_t stream) {
-    DecArgs a;
+                          hipStream_t stream, const MoeSortFuse *fuse) {
+    DecArgs a = {};
     a.act = act;
     a.sorted_tok = sorted_tok;
     a.offsets = offsets;
@@ -815,6 +917,12 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
     if ((int64_t)cap * ((a.units + G - 1) / G) > 2 * (int64_t)nblk &&
         max_passes * a.units * 7 < ((int64_t)1 << 31)) {
+        if (fuse) {
+            const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
+                                           fuse->pair_pos, fuse->active, fuse->active_count, fuse->err_flag,
+                                           stream);
+            if (rc != MOE_NVFP4_OK) return rc;
+        }
         if (gated)
             hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
         else
@@ -826,6 +934,28 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     int extra = (P - 1) / pr;
     if (extra > 64) extra = 64;
     a.extra = extra;
+    if (fuse) {
+        // The routing sort runs inside this launch when every expert's rows
+        // fit one pass (no further-pass block rows) and the pairs fit a wave.
+        if (gated && extra == 0 && P <= kSortPairs) {
+            a.fused_sort = 1;
+            a.P = P;
+            a.topk = fuse->k;
+            a.E = E;
+            a.topk_ids = fuse->topk_ids;
+            a.sort_offsets = fuse->offsets;
+            a.sort_tok = fuse->sorted_tok;
+            a.sort_pos = fuse->pair_pos;
+            a.sort_active = fuse->active;
+            a.sort_count = fuse->active_count;
+            a.err_flag = fuse->err_flag;
+        } else {
+            const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
+                                           fuse->pair_pos, fuse->active, fuse->active_count, fuse->err_flag,
+                                           stream);
+            if (rc != MOE_NVFP4_OK) return rc;
+        }
+    }
     dim3 grid((unsigned)((a.units + G - 1) / G), (unsigned)(cap + extra));
     if (gated)
         hipLaunchKernelGGL(k_decode_row<true>, grid, dim3(kThreads), lds, stream, a);

@@ -18,18 +18,6 @@
 
 namespace {
 
-// Mask of the lanes whose id equals this lane's (among lanes with valid set),
-// from one ballot per id bit.
-__device__ __forceinline__ unsigned long long match_lanes(int e, bool valid, int nbits) {
-    unsigned long long eq = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const unsigned long long m = __ballot(valid && bit);
-        eq &= bit ? m : ~m;
-    }
-    return eq;
-}
-
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / moe::kWave;
 constexpr int kIdsPerLane = 8;
@@ -104,7 +92,7 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
             const bool valid = f < f1 && e >= 0 && e < E;
             bad |= f < f1 && !valid;
             // The first lane of each id adds the group's count.
-            const unsigned long long eq = match_lanes(e, valid, nbits);
+            const unsigned long long eq = moe::match_lanes(e, valid, nbits);
             if (valid && (eq & lt) == 0ull) my[e] += __popcll(eq);
         }
     }
@@ -148,7 +136,7 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
             const bool in = f < f1;
             const int e = ev[j];
             const bool valid = in && e >= 0 && e < E;
-            const unsigned long long eq = match_lanes(e, valid, nbits);
+            const unsigned long long eq = moe::match_lanes(e, valid, nbits);
             const int rank = __popcll(eq & lt), same = __popcll(eq);
             int pos = -1;
             if (valid) pos = my[e] + rank;
@@ -240,7 +228,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     if (wave == 0) {
         // Stable rank among equal ids: lanes are in flat pair order.
         const unsigned long long lt = (1ull << lane) - 1ull;
-        const int rank = __popcll(match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
+        const int rank = __popcll(moe::match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
         if (tid < P) {
             const int pos = valid ? cnt[e] + rank : -1;
             pair_pos[tid] = pos;
@@ -252,6 +240,22 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
 
 }  // namespace
 
+// The sort launch itself (arguments already checked).
+int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *expert_offsets,
+                    int32_t *sorted_token_ids, int32_t *pair_pos, int32_t *active_experts, int32_t *active_count,
+                    uint32_t *err_flag, hipStream_t stream) {
+    const int P = T * k;
+    if (P <= kSmallPairs) {
+        hipLaunchKernelGGL(k_moe_sort_small, dim3(1), dim3(kSmallThreads), 0, stream, topk_ids, P, k, E,
+                           expert_offsets, sorted_token_ids, pair_pos, active_experts, active_count, err_flag);
+        return moe_host::launch_status();
+    }
+    const size_t lds = (size_t)kSortWaves * E * sizeof(int);
+    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), lds, stream, topk_ids, P, k, E, expert_offsets,
+                       sorted_token_ids, pair_pos, active_experts, active_count, err_flag);
+    return moe_host::launch_status();
+}
+
 extern "C" int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
                               int32_t *expert_offsets, int32_t *sorted_token_ids, int32_t *pair_pos,
                               int32_t *active_experts, int32_t *active_count, uint32_t *err_flag,
@@ -261,17 +265,8 @@ extern "C" int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int
         return MOE_NVFP4_ENULL;
     if (T < 1 || k < 1 || E < 1 || k > E) return MOE_NVFP4_ESHAPE;
     if (E > MOE_NVFP4_MAX_EXPERTS || (int64_t)T * k > MOE_NVFP4_MAX_PAIRS) return MOE_NVFP4_ELIMIT;
-    const int P = T * k;
-    if (P <= kSmallPairs) {
-        hipLaunchKernelGGL(k_moe_sort_small, dim3(1), dim3(kSmallThreads), 0, (hipStream_t)stream, topk_ids, P, k,
-                           E, expert_offsets, sorted_token_ids, pair_pos, active_experts, active_count, err_flag);
-        return moe_host::launch_status();
-    }
-    const size_t lds = (size_t)kSortWaves * E * sizeof(int);
-    hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(kSortThreads), lds, (hipStream_t)stream, topk_ids, P,
-                       k, E, expert_offsets, sorted_token_ids, pair_pos, active_experts, active_count,
-                       err_flag);
-    return moe_host::launch_status();
+    return moe_launch_sort(topk_ids, T, k, E, expert_offsets, sorted_token_ids, pair_pos, active_experts,
+                           active_count, err_flag, (hipStream_t)stream);
 }
 
 extern "C" int moe_nvfp4_abi_version(void) { return MOE_NVFP4_ABI_VERSION; }

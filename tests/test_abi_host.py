@@ -17,10 +17,10 @@ def test_library_exports_every_header_function():
     names = moe.header_functions()
     assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                           "transpose_u8", "moe_nvfp4_abi_version", "moe_nvfp4_route", "transpose_u8_pitched",
-                          "moe_nvfp4_gate_up_silu_concat"}
+                          "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 3
+    assert L.moe_nvfp4_abi_version() == 4
 
 
 def _ex(layout=0, null=False):
@@ -121,3 +121,19 @@ def test_concat_gate_up_and_pitched_transpose_reject():
     assert L.transpose_u8_pitched(D, D, 4, 4, 3, None) == ESHAPE    # pitch < rows
     assert L.transpose_u8_pitched(D, D, 0, 4, 4, None) == ESHAPE
     assert L.transpose_u8_pitched(D, D, 4, 1 << 30, 1 << 12, None) == ELIMIT
+
+
+def test_sort_gate_up_rejects():
+    L = moe.lib()
+
+    def call(ids=D, x=D, T=4, k=2, E=4, H=256, I=512, g=None, u=None, err=D, h=D):
+        return L.moe_nvfp4_sort_gate_up_silu(ids, x, T, k, E, H, I, g or _ex(), u or _ex(), D, D, D, D, D, err, h,
+                                             None)
+
+    assert call(ids=None) == ENULL
+    assert call(err=None) == ENULL
+    assert call(h=None) == ENULL
+    assert call(g=_ex(0), u=_ex(1)) == ELAYOUT
+    assert call(k=5) == ESHAPE                          # k > E
+    assert call(H=192) == ESHAPE                        # row-major needs H >= 256
+    assert call(E=2000) == ELIMIT

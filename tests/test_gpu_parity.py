@@ -480,3 +480,49 @@ def test_ragged_concat_gate_up(T, H, I, E, k, fmt):
     say("ragged concat", T, H, I, E, k, fmt)
     shape = synth.MoeShape(f"ragged_cc_{T}_{H}_{I}_{E}_{k}", T, H, I, E, k, "uniform", True)
     _full_check(Case(23, shape, fmt=fmt, concat=True, nulls=(1,)), f"ragged concat {T},{H},{I},{E},{k},{fmt}")
+
+
+# ---------------------------------------------------------------- sort fused into the gate+up launch
+@pytest.mark.parametrize("T,k,E,H,I,mode", [(1, 8, 128, 2048, 768, "rand"), (4, 2, 4, 256, 512, "rand"),
+                                             (2, 8, 1024, 256, 256, "invalid"), (3, 5, 7, 512, 256, "dup"),
+                                             (16, 3, 4, 512, 256, "dup"), (2, 32, 64, 256, 384, "rand"),
+                                             (32, 6, 128, 2688, 1856, "rand")])
+def test_sort_fused_into_gate_up_matches_two_calls(T, k, E, H, I, mode):
+    """moe_nvfp4_sort_gate_up_silu (one launch while P <= 64 and each expert
+    fits one pass; two launches otherwise) against the two separate calls:
+    sort outputs and err_flag equal, h bit for bit; sort outputs against the
+    oracle's brute force."""
+    say("fused sort", T, k, E, H, I, mode)
+    shape = synth.MoeShape(f"fs_{T}_{k}_{E}", T, H, I, E, k, "uniform", False)
+    rng = np.random.default_rng(T * 1000 + E)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    if mode == "dup":
+        ids[:, 1] = ids[:, 0]
+    if mode == "invalid":
+        ids[0, 0] = -1
+        ids[-1, -1] = E + 3
+    case = Case(24, shape, ids=ids)
+    L = case.layer
+    outs = []
+    for fused in (True, False):
+        L.err_flag.zero_()
+        L.h.fill_(7.0)
+        L.expert_offsets.fill_(-5)
+        if fused:
+            moe.moe_nvfp4_sort_gate_up_silu(case.ids_d, case.x, E, H, I, L.gate, L.up, L.expert_offsets,
+                                            L.sorted_token_ids, L.pair_pos, L.active_experts, L.active_count,
+                                            L.err_flag, L.h)
+        else:
+            moe.moe_nvfp4_sort(case.ids_d, E, L.expert_offsets, L.sorted_token_ids, L.pair_pos, L.active_experts,
+                               L.active_count, L.err_flag)
+            moe.moe_nvfp4_gate_up_silu(case.x, k, E, H, I, L.gate, L.up, L.expert_offsets, L.sorted_token_ids,
+                                       L.active_experts, L.active_count, L.h)
+        torch.cuda.synchronize()
+        outs.append((case.sort_outputs(), L.h.clone()))
+    (s_f, h_f), (s_u, h_u) = outs
+    for key in ("expert_offsets", "sorted_token_ids", "pair_pos", "active_experts"):
+        assert np.array_equal(s_f[key], s_u[key]), key
+    assert s_f["active_count"] == s_u["active_count"] and s_f["err"] == s_u["err"]
+    _check_sort(case, oracle.sort_routes(case.ids, E))
+    n = int(s_u["expert_offsets"][-1])
+    assert torch.equal(h_f[:n], h_u[:n])
