@@ -526,3 +526,32 @@ def test_sort_fused_into_gate_up_matches_two_calls(T, k, E, H, I, mode):
     _check_sort(case, oracle.sort_routes(case.ids, E))
     n = int(s_u["expert_offsets"][-1])
     assert torch.equal(h_f[:n], h_u[:n])
+
+
+# ---------------------------------------------------------------- graph capture
+def test_layer_graph_replays_match_eager():
+    """The decode layer (sort fused into gate+up) captured in a HIP graph: every
+    replay, with eager work and synchronisations between replays, gives the
+    eager result bit for bit."""
+    say("graph replay, 1-token decode layer")
+    case = Case(2)
+    L = case.layer
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        L.forward(case.x, case.ids_d, case.w_d, stream=stream)
+    torch.cuda.synchronize()
+    eager_out, eager_h = L.out.clone(), L.h.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        L.forward(case.x, case.ids_d, case.w_d, stream=stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        L.out.fill_(9.0)
+        L.h.fill_(9.0)
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(L.out, eager_out), rep
+        assert torch.equal(L.h[: case.shape.P], eager_h[: case.shape.P]), rep
+        del scratch
