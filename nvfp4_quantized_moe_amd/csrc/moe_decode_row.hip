@@ -911,11 +911,15 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     if (pr > P) pr = P;
     a.pass_rows = pr;
     const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
-    // Persistent mode when the grid would hold many blocks per resident slot
-    // and the weighted work count fits an int.
+    // Persistent mode for gate+up when the grid would hold many blocks per
+    // resident slot and the weighted work count fits an int.  (The down
+    // projection measured faster as one block per unit group: with its
+    // shorter rows (K = I) a persistent block crosses more pass boundaries,
+    // each a fresh activation stage and ring fill, 5% on 64 tokens x 256
+    // experts.)
     const int nblk = 2 * moe_host::cu_count();
     const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
-    if ((int64_t)cap * ((a.units + G - 1) / G) > 2 * (int64_t)nblk &&
+    if (gated && (int64_t)cap * ((a.units + G - 1) / G) > 2 * (int64_t)nblk &&
         max_passes * a.units * 7 < ((int64_t)1 << 31)) {
         if (fuse) {
             const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
@@ -923,10 +927,7 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
                                            stream);
             if (rc != MOE_NVFP4_OK) return rc;
         }
-        if (gated)
-            hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
-        else
-            hipLaunchKernelGGL(k_decode_row_persist<false>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
         return moe_host::launch_status();
     }
     // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
