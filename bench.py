@@ -4,7 +4,8 @@
                     [--gate-up separate|concat]
 
 A step is one MoE layer forward through the whole path — routing sort,
-gate+up+SiLU, down, blend — over one batch of synthetic input.  Every input
+gate+up+SiLU, down, blend — over one batch of synthetic input (at a few
+tokens the sort runs inside the gate+up launch).  Every input
 is resident in HBM before timing starts.  Consecutive steps run different
 layers' expert weights (separate HBM copies, as successive layers of a model
 would), so the weights a step reads were last touched far more than the
@@ -15,8 +16,10 @@ a device synchronisation on each side (``--eager`` launches them one by one
 instead).  Reported on one JSON line:
   value       expert-weight bytes of the active experts per step / step time (GB/s)
   tokens_per_s, pct_of_hbm_peak
-  roofline    the dominant kernel (gate+up+SiLU): its algorithmic bytes per
-              launch / its mean launch duration, timed with HIP events on the
+  roofline    the dominant kernel (gate+up+SiLU, with the routing sort fused
+              in where the step runs it that way: one token): its
+              algorithmic bytes per launch / its mean launch duration, timed
+              with HIP events on the
               stream it runs on, against 8 TB/s (the many-token K-major
               workload: its flops per launch against the 2.5 PFLOP/s bf16/fp16
               matrix-core peak); traffic = HBM bytes per launch from the
@@ -263,9 +266,18 @@ def main():
     bufs = moe.MoeLayer(shape.T, shape.k, shape.E, shape.H, shape.I, *layers[0][1], device=dev,
                         gate_up=layers[0][2], pitch=pitch)
 
+    # The gate+up launch the step runs: at few tokens the sort is fused into
+    # it (one kernel), which is then the launch timed and profiled.
+    fused_sort = (not concat) and moe.moe_nvfp4_sort_gate_up_launches(shape.T, shape.k, shape.E, shape.H, shape.I,
+                                                                      layout) == 1
+
     def gate_up_launch(li, s):
         tabs, gu = layers[li % L][1], layers[li % L][2]
-        if gu is not None:
+        if fused_sort:
+            moe.moe_nvfp4_sort_gate_up_silu(ids_d[0], xs[0], shape.E, shape.H, shape.I, tabs[0], tabs[1],
+                                            bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
+                                            bufs.active_experts, bufs.active_count, bufs.err_flag, bufs.h, s)
+        elif gu is not None:
             moe.moe_nvfp4_gate_up_silu_concat(xs[0], shape.k, shape.E, shape.H, shape.I, gu, pitch,
                                               bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
                                               bufs.active_count, bufs.h, s)
@@ -354,7 +366,7 @@ def main():
             e1.record(stream)
     torch.cuda.synchronize()
     gu_ms = e0.elapsed_time(e1) / Kr
-    gu_bytes = float(gate_up_bytes(shape, idss[0], group))
+    gu_bytes = float(gate_up_bytes(shape, idss[0], group)) + (shape.P * 4 if fused_sort else 0)
     traffic = measured_traffic(shape.name)
     if shape.kmajor:
         # Many-token path: a dense bf16 contraction on the matrix cores.
@@ -367,7 +379,8 @@ def main():
         achieved = gu_bytes / (gu_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": traffic, "kernel": "moe_nvfp4_gate_up_silu", "launch_us": round(gu_ms * 1e3, 3),
+    kname = "moe_nvfp4_sort_gate_up_silu (sort fused in)" if fused_sort else "moe_nvfp4_gate_up_silu"
+    roof.update({"traffic": traffic, "kernel": kname, "launch_us": round(gu_ms * 1e3, 3),
                  "algorithmic_bytes_per_launch": round(gu_bytes)})
 
     # ---- the router ahead of the path (softmax, top-k, renormalise), timed

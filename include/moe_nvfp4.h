@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 4
+#define MOE_NVFP4_ABI_VERSION 5
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
 #define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
@@ -178,6 +178,16 @@ int moe_nvfp4_sort_gate_up_silu(const int32_t *topk_ids, const uint16_t *x, int3
                                 int32_t *sorted_token_ids, int32_t *pair_pos,
                                 int32_t *active_experts, int32_t *active_count, uint32_t *err_flag,
                                 float *h, void *stream);
+
+/*
+ * moe_nvfp4_sort_gate_up_launches — how many launches
+ * moe_nvfp4_sort_gate_up_silu enqueues for these sizes and layout on the
+ * current device: 1 (the sort runs inside the gate+up launch) or 2.  Host
+ * only; no device work.  Errors as moe_nvfp4_gate_up_silu's size and layout
+ * checks.
+ */
+int moe_nvfp4_sort_gate_up_launches(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                    int32_t layout);
 
 /*
  * moe_nvfp4_gate_up_silu_concat — moe_nvfp4_gate_up_silu over a

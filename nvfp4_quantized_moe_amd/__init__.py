@@ -42,6 +42,7 @@ __all__ = [
     "transpose_concat_for_gemm",
     "moe_nvfp4_gate_up_silu_concat",
     "moe_nvfp4_sort_gate_up_silu",
+    "moe_nvfp4_sort_gate_up_launches",
     "moe_nvfp4_route",
     "with_shared_expert",
 ]
@@ -98,9 +99,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_gate_up_silu_concat.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _I, _P, _P, _P, _P, _P, _P]
         L.moe_nvfp4_sort_gate_up_silu.argtypes = [_P, _P, _I, _I, _I, _I, _I, _Experts, _Experts, _P, _P, _P, _P,
                                                   _P, _P, _P, _P]
+        L.moe_nvfp4_sort_gate_up_launches.argtypes = [_I, _I, _I, _I, _I, _I]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                    "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version", "transpose_u8_pitched",
-                   "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu"):
+                   "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
+                   "moe_nvfp4_sort_gate_up_launches"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,6 +218,14 @@ def moe_nvfp4_sort_gate_up_silu(topk_ids, x, E, H, I, gate: ExpertTables, up: Ex
         _dev(err_flag, torch.int32, "err_flag"),
         _dev(h, torch.float32, "h"), _stream(stream))
     _check("moe_nvfp4_sort_gate_up_silu", rc)
+
+
+def moe_nvfp4_sort_gate_up_launches(T, k, E, H, I, layout) -> int:
+    """1 when moe_nvfp4_sort_gate_up_silu runs as one launch for these sizes, else 2."""
+    rc = lib().moe_nvfp4_sort_gate_up_launches(T, k, E, H, I, layout)
+    if rc < 0:
+        raise MoeNvfp4Error("moe_nvfp4_sort_gate_up_launches", rc)
+    return rc
 
 
 def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, expert_offsets,

@@ -10,6 +10,7 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
                           hipStream_t stream, const MoeSortFuse *fuse);
+int moe_decode_sort_gate_up_launches(int N, int K, int P, int E);
 int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets, int32_t *sorted_tok,
                     int32_t *pair_pos, int32_t *active, int32_t *active_count, uint32_t *err_flag,
                     hipStream_t stream);
@@ -80,6 +81,14 @@ extern "C" int moe_nvfp4_sort_gate_up_silu(const int32_t *topk_ids, const uint16
     if (src != MOE_NVFP4_OK) return src;
     return moe_launch_gemm_kmajor(true, gate.layout == MOE_NVFP4_K_MAJOR_MXFP4, x, sorted_token_ids,
                                   expert_offsets, active_experts, active_count, gate, &up, h, I, H, P, E, I, 0, st);
+}
+
+extern "C" int moe_nvfp4_sort_gate_up_launches(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                               int32_t layout) {
+    const int rc = check_common(T, k, E, H, I, layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    if (layout != MOE_NVFP4_ROW_MAJOR) return 2;
+    return moe_decode_sort_gate_up_launches(I, H, T * k, E);
 }
 
 extern "C" int moe_nvfp4_gate_up_silu_concat(const uint16_t *x, int32_t T, int32_t k, int32_t E, int32_t H,

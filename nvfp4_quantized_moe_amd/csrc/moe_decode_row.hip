@@ -708,7 +708,7 @@ __device__ __forceinline__ int3 fused_sort(const DecArgs &a, SortLds *sl, int sl
 //   y <  extra: further passes number y, y + extra, ... in slot order, so an
 //               expert with many routed rows is spread over many blocks of
 //               about the same length as the rest.
-template <bool GATED>
+template <bool GATED, bool SORT>  // SORT: gate+up with the routing sort fused in (fused_sort set)
 __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     extern __shared__ uint4 lds4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
@@ -716,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     const int nu = min(a.G, a.units - u_first);
     if (nu <= 0) return;
     const int y = blockIdx.y;
-    if (GATED && a.fused_sort) {  // extra == 0: one pass per expert
+    if constexpr (GATED && SORT) {  // extra == 0: one pass per expert
         const int3 r = fused_sort(a, reinterpret_cast<SortLds *>(lds + kPreOff), y);
         if (r.x < 0) return;  // past the active count
         do_pass_rows<GATED, true>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, lds);
@@ -869,6 +869,71 @@ int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *offse
                     int32_t *pair_pos, int32_t *active, int32_t *active_count, uint32_t *err_flag,
                     hipStream_t stream);
 
+namespace {
+
+// Launch shape of the decode kernels for one projection (shared by the
+// launcher and the fusion query below).
+struct DecConfig {
+    int units, G, ldx, pass_rows, extra;
+    size_t lds;
+    bool persistent;
+    bool ok;  // false: an activation row does not fit the LDS budget
+};
+
+DecConfig decode_config(bool gated, int N, int K, int P, int E) {
+    DecConfig c{};
+    const int ucols = gated ? 16 : 32;
+    c.units = (N + ucols - 1) / ucols;
+    const int cap = E < P ? E : P;
+    // Units per block: about 32 ring steps per wave, so a block's start-up
+    // (tables, activation staging, first loads) is paid over enough streaming;
+    // fewer when the grid would otherwise not fill two blocks per CU.
+    const int nseg = (K / 2 + 255) / 256;
+    int G = (32 + nseg - 1) / nseg;
+    G = G < 1 ? 1 : (G > 8 ? 8 : G);
+    while (G > 1 && (int64_t)cap * ((c.units + G - 1) / G) < 2 * (int64_t)moe_host::cu_count()) --G;
+    c.G = G;
+    // Staged row stride: 2K bytes padded to 16 mod 256, so the 16 lanes of an
+    // A-operand read (4 rows x 4 quarters, 64 bytes apart) hit distinct banks.
+    const int pad_bytes = ((16 - (2 * K) % 256) + 256) % 256;
+    c.ldx = K + pad_bytes / 2;
+    const size_t row_lds = (size_t)c.ldx * 2;
+    int pr = (int)(kLdsBudget / row_lds);
+    c.ok = pr >= 1;
+    if (pr > 4 * kMaxTG) pr = 4 * kMaxTG;
+    if (pr > P) pr = P;
+    if (pr < 1) pr = 1;
+    c.pass_rows = pr;
+    c.lds = (size_t)kHdrLds + (size_t)pr * row_lds;
+    // Persistent mode for gate+up when the grid would hold many blocks per
+    // resident slot and the weighted work count fits an int.  (The down
+    // projection measured faster as one block per unit group: with its
+    // shorter rows (K = I) a persistent block crosses more pass boundaries,
+    // each a fresh activation stage and ring fill, 5% on 64 tokens x 256
+    // experts.)
+    const int nblk = 2 * moe_host::cu_count();
+    const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
+    c.persistent = gated && (int64_t)cap * ((c.units + G - 1) / G) > 2 * (int64_t)nblk &&
+                   max_passes * c.units * 7 < ((int64_t)1 << 31);
+    // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
+    // the grid's y extent is kept within its limit by striding over them.
+    int extra = (P - 1) / pr;
+    c.extra = extra > 64 ? 64 : extra;
+    return c;
+}
+
+// The routing sort runs inside the gate+up launch when every expert's rows
+// fit one pass (no further-pass block rows) and the pairs fit a wave.
+bool decode_sort_fuses(const DecConfig &c, int P) { return !c.persistent && c.extra == 0 && P <= kSortPairs; }
+
+}  // namespace
+
+// Launches that moe_nvfp4_sort_gate_up_silu enqueues for row-major weights (1
+// when the sort runs inside the gate+up launch, else 2).
+int moe_decode_sort_gate_up_launches(int N, int K, int P, int E) {
+    return decode_sort_fuses(decode_config(true, N, K, P, E), P) ? 1 : 2;
+}
+
 int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok, const int32_t *offsets,
                           const int32_t *active, const int32_t *nactive, const moe_nvfp4_experts &A,
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
@@ -889,38 +954,17 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.N = N;
     a.K = K;
     a.single_token = gated && T == 1;
-    const int ucols = gated ? 16 : 32;
-    a.units = (N + ucols - 1) / ucols;
-    const int cap = E < P ? E : P;
-    // Units per block: about 32 ring steps per wave, so a block's start-up
-    // (tables, activation staging, first loads) is paid over enough streaming;
-    // fewer when the grid would otherwise not fill two blocks per CU.
-    const int nseg = (K / 2 + 255) / 256;
-    int G = (32 + nseg - 1) / nseg;
-    G = G < 1 ? 1 : (G > 8 ? 8 : G);
-    while (G > 1 && (int64_t)cap * ((a.units + G - 1) / G) < 2 * (int64_t)moe_host::cu_count()) --G;
-    a.G = G;
-    // Staged row stride: 2K bytes padded to 16 mod 256, so the 16 lanes of an
-    // A-operand read (4 rows x 4 quarters, 64 bytes apart) hit distinct banks.
-    const int pad_bytes = ((16 - (2 * K) % 256) + 256) % 256;
-    a.ldx = K + pad_bytes / 2;
-    const size_t row_lds = (size_t)a.ldx * 2;
-    int pr = (int)(kLdsBudget / row_lds);
-    if (pr < 1) return MOE_NVFP4_ELIMIT;
-    if (pr > 4 * kMaxTG) pr = 4 * kMaxTG;
-    if (pr > P) pr = P;
-    a.pass_rows = pr;
-    const size_t lds = (size_t)kHdrLds + (size_t)pr * row_lds;
-    // Persistent mode for gate+up when the grid would hold many blocks per
-    // resident slot and the weighted work count fits an int.  (The down
-    // projection measured faster as one block per unit group: with its
-    // shorter rows (K = I) a persistent block crosses more pass boundaries,
-    // each a fresh activation stage and ring fill, 5% on 64 tokens x 256
-    // experts.)
+    const DecConfig c = decode_config(gated, N, K, P, E);
+    if (!c.ok) return MOE_NVFP4_ELIMIT;
+    a.units = c.units;
+    a.G = c.G;
+    a.ldx = c.ldx;
+    a.pass_rows = c.pass_rows;
+    const size_t lds = c.lds;
+    const int G = c.G;
     const int nblk = 2 * moe_host::cu_count();
-    const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
-    if (gated && (int64_t)cap * ((a.units + G - 1) / G) > 2 * (int64_t)nblk &&
-        max_passes * a.units * 7 < ((int64_t)1 << 31)) {
+    const int cap = E < P ? E : P;
+    if (c.persistent) {
         if (fuse) {
             const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
                                            fuse->pair_pos, fuse->active, fuse->active_count, fuse->err_flag,
@@ -930,15 +974,10 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
         hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
         return moe_host::launch_status();
     }
-    // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
-    // the grid's y extent is kept within its limit by striding over them.
-    int extra = (P - 1) / pr;
-    if (extra > 64) extra = 64;
+    const int extra = c.extra;
     a.extra = extra;
     if (fuse) {
-        // The routing sort runs inside this launch when every expert's rows
-        // fit one pass (no further-pass block rows) and the pairs fit a wave.
-        if (gated && extra == 0 && P <= kSortPairs) {
+        if (gated && decode_sort_fuses(c, P)) {
             a.fused_sort = 1;
             a.P = P;
             a.topk = fuse->k;
@@ -958,9 +997,11 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
         }
     }
     dim3 grid((unsigned)((a.units + G - 1) / G), (unsigned)(cap + extra));
-    if (gated)
-        hipLaunchKernelGGL(k_decode_row<true>, grid, dim3(kThreads), lds, stream, a);
+    if (gated && a.fused_sort)
+        hipLaunchKernelGGL((k_decode_row<true, true>), grid, dim3(kThreads), lds, stream, a);
+    else if (gated)
+        hipLaunchKernelGGL((k_decode_row<true, false>), grid, dim3(kThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL(k_decode_row<false>, grid, dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((k_decode_row<false, false>), grid, dim3(kThreads), lds, stream, a);
     return moe_host::launch_status();
 }

@@ -17,10 +17,11 @@ def test_library_exports_every_header_function():
     names = moe.header_functions()
     assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                           "transpose_u8", "moe_nvfp4_abi_version", "moe_nvfp4_route", "transpose_u8_pitched",
-                          "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu"}
+                          "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
+                          "moe_nvfp4_sort_gate_up_launches"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 4
+    assert L.moe_nvfp4_abi_version() == 5
 
 
 def _ex(layout=0, null=False):
@@ -137,3 +138,12 @@ def test_sort_gate_up_rejects():
     assert call(k=5) == ESHAPE                          # k > E
     assert call(H=192) == ESHAPE                        # row-major needs H >= 256
     assert call(E=2000) == ELIMIT
+
+
+def test_sort_gate_up_launch_count_query():
+    """Host-only query (no GPU work): K-major always sorts in its own launch;
+    bad sizes are rejected like the projection's own checks."""
+    L = moe.lib()
+    assert L.moe_nvfp4_sort_gate_up_launches(2048, 4, 64, 4096, 1536, 1) == 2
+    assert L.moe_nvfp4_sort_gate_up_launches(4, 2, 4, 256, 512, 7) == ELAYOUT
+    assert L.moe_nvfp4_sort_gate_up_launches(4, 5, 4, 256, 512, 0) == ESHAPE
