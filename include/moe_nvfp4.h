@@ -145,7 +145,9 @@ int moe_nvfp4_sort(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
  *   h                 out fp32 [P, I]; rows of positions that belong to no
  *                     active expert are left untouched.
  * Admission: H % 64 == 0 and I % 64 == 0 (both layouts), H >= 256 and
- * I >= 256 (ROW_MAJOR); packed, scale and activation buffers 16-byte
+ * I >= 256 (ROW_MAJOR); ROW_MAJOR also K <= 36736 (K = H here, I for the
+ * down projection: the decode kernel stages whole activation rows in its
+ * shared memory), ELIMIT above; packed, scale and activation buffers 16-byte
  * aligned; K_MAJOR(_MXFP4): the activation tensor (x here, h for the down
  * projection) below 4 GiB.  The K-major path feeds the matrix cores with
  * bf16 operands (x as given, the decoded weights exactly), so it admits the

@@ -61,6 +61,7 @@ def test_gate_up_rejects():
     assert call(I=528, g=_ex(1), u=_ex(1)) == ESHAPE    # K-major needs I % 64 == 0
     assert call(k=5) == ESHAPE
     assert call(H=1 << 17) == ELIMIT
+    assert call(H=36800) == ELIMIT                      # a row-major x row must fit the decode kernel's LDS
     # K-major: x of 4 GiB or more (activation offsets are 32-bit)
     assert call(T=1 << 16, H=1 << 15, g=_ex(1), u=_ex(1)) == ELIMIT
     assert call(T=1 << 16, H=1 << 15, g=_ex(2), u=_ex(2)) == ELIMIT

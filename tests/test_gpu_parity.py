@@ -88,8 +88,10 @@ def test_sort_configs_bit_exact(cfg):
 @pytest.mark.parametrize("T,k,E,mode", [(1, 1, 1, "rand"), (3, 4, 5, "dup"), (9, 3, 7, "invalid"),
                                          (16384, 8, 256, "rand"), (2048, 4, 1024, "rand"), (512, 1, 1024, "skew"),
                                          (100, 8, 8, "all_same"), (1000, 3, 50, "rand"),
-                                         (5000, 7, 300, "invalid")])
+                                         (5000, 7, 300, "invalid"), (1 << 19, 8, 1024, "rand")])
 def test_sort_edge_cases_bit_exact(T, k, E, mode):
+    """Includes the maximum sizes: 2^22 pairs (MOE_NVFP4_MAX_PAIRS) over 1024
+    experts (MOE_NVFP4_MAX_EXPERTS)."""
     say("sort edge", T, k, E, mode)
     rng = np.random.default_rng(T * 31 + k * 7 + E)
     ids = rng.integers(0, E, (T, k)).astype(np.int32)
@@ -555,3 +557,18 @@ def test_layer_graph_replays_match_eager():
         assert torch.equal(L.out, eager_out), rep
         assert torch.equal(L.h[: case.shape.P], eager_h[: case.shape.P]), rep
         del scratch
+
+
+# ---------------------------------------------------------------- widest admitted rows
+@pytest.mark.parametrize("kmajor,H", [(False, 36736), (True, 65536)])
+def test_widest_hidden_width(kmajor, H):
+    """The widest activation rows each path admits: the decode kernel stages
+    one row of x (fp16) in its LDS budget, so K = H <= 36736; the K-major GEMM
+    takes the full MOE_NVFP4_MAX_WIDTH = 65536.  (I = 256: with a 64-wide
+    down projection and 393K outputs, the tail of the bf16 rounding of h
+    before the K-major down GEMM reaches 1.11 of the strict bound, the
+    official one holding at 0.006; 64-wide down projections are covered at
+    fewer outputs by the ragged MXFP4 shapes.)"""
+    say("widest H", H, "kmajor" if kmajor else "row")
+    shape = synth.MoeShape(f"wide_h_{H}", 6, H, 256, 2, 1, "uniform", kmajor)
+    _full_check(Case(25, shape), f"widest H {H}")
