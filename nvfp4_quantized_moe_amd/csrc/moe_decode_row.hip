@@ -70,6 +70,7 @@ constexpr int kRmaxOff = kWaves * kScaleLds;                    // per-row maxim
 constexpr int kPreOff = kRmaxOff + 64;
 constexpr int kHdrLds = kPreOff + kPreLds;  // scale areas + row maxima + pass prefix; then the rows
 
+using moe::u32x2_t;
 using moe::u32x4_t;
 // sched_barrier mask: ALU, VALU, SALU, MFMA, LDS and transcendental
 // instructions may be scheduled across; global memory instructions may not.
@@ -550,6 +551,206 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     for (int d = 0; d < D; ++d) step(d, std::false_type{});
 }
 
+// Token-dense pass, for passes of more than 8 rows.  The (row, quarter)
+// layout above feeds 4 tokens per MFMA and keeps a quarter of each result,
+// so a pass of 16 rows costs 4 MFMAs per decoded operand; here one MFMA
+// takes all 16 rows of the pass.  Each B column is one weight row: lane
+// (n, q) loads 16 bytes (32 k) of row n at byte 64 window + 16 q, so a load
+// instruction reads 16 rows x 64 contiguous bytes (streams within a few
+// percent of 4 rows x 256 bytes).  MFMA d of a window takes dword d of every
+// lane, i.e. k = 128 window + 32 q + 8 d + i in B slot (q, i); the A operand
+// (x rows of the pass, staged as above) is read at the same k.  The k order
+// inside the sum differs from the plain order; the products do not.
+//   * A wave owns whole units (gate+up: the 16 gate and 16 up rows of 16
+//     output columns; down: 32 output rows as two groups of 16), taking the
+//     block's units round-robin; a step is one 64-byte window of its two
+//     16-row groups.
+//   * Scales: every 4 steps each lane loads the 8 scale bytes of one (step,
+//     group, row) into the wave's 1 KiB LDS area; a step reads its two bytes
+//     per lane from there.
+template <bool GATED, int D, bool TOK_LDS>
+__device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int pr, int u_first, int nu,
+                                               const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
+                                               const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
+    static_assert(D % kGroup == 0, "ring depth");
+    const int K = a.K, N = a.N, ldx = a.ldx;
+    const int rowbytes = K >> 1, sbytes = K >> 4;
+    const int nwin = (rowbytes + 63) >> 6;  // 64-byte windows (128 k) per row
+    const int lane = threadIdx.x & 63, w = moe::wave_id();
+    const int n = lane & 15, q = lane >> 4;
+    const int nuw = nu > w ? (nu - w + 3) >> 2 : 0;  // units of this wave: u_first + w + 4 j
+    const int total = nuw * nwin;
+    // Unit read past the end of this wave's list (a wave with none reads the
+    // block's first unit): the addresses stay inside the expert's weights.
+    const int last_unit = nuw > 0 ? u_first + w + 4 * (nuw - 1) : u_first;
+    // Scale-load role: step s4 of the group, row n of group sg.
+    const int s4 = lane >> 4, sg = (lane >> 3) & 1;
+    // (lanes 0..63 cover 4 steps x 2 groups x 8 rows per load; two loads per
+    //  group cover the 16 rows: row n8 + 8 h)
+    const int n8 = lane & 7;
+
+    uint8_t *sc_lds = lds + w * kScaleLds;
+    uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kRmaxOff);
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds + kHdrLds);
+
+    // Row bases of this lane's two weight rows in unit 0, and the unit stride.
+    const uint8_t *wb0 = pA + (size_t)n * rowbytes;
+    const uint8_t *wb1 = GATED ? pB + (size_t)n * rowbytes : pA + (size_t)(16 + n) * rowbytes;
+    const size_t ustride = (size_t)(GATED ? 16 : 32) * rowbytes;
+    // Scale rows loaded by this lane (rows n8 and n8 + 8 of group sg), unit 0.
+    const uint8_t *sgb = sg == 0 ? sA : (GATED ? sB : sA);
+    const int sgrow0 = (GATED || sg == 0) ? 0 : 16;
+    const uint8_t *sbase0 = sgb + (size_t)(sgrow0 + n8) * sbytes;
+    const uint8_t *sbase1 = sgb + (size_t)(sgrow0 + n8 + 8) * sbytes;
+    const size_t sustride = (size_t)(GATED ? 16 : 32) * sbytes;
+
+    u32x4_t w0[D], w1[D];
+    u32x2_t sv0[D / kGroup], sv1[D / kGroup];
+    int ssh0[D / kGroup], ssh1[D / kGroup];  // dword shift of a clamped scale load
+    int lj = 0, lw = 0;                      // stream position of the next load (unit, window)
+    auto load = [&](int d) {
+        if (d % kGroup == 0) {
+            // Scales of step (lj, lw) + s4: 8 bytes of window l for rows n8, n8 + 8 of group sg.
+            int l = lw + s4, j = lj;
+#pragma unroll
+            for (int i = 0; i < kGroup - 1; ++i) {
+                const bool wrap = l >= nwin;
+                l = wrap ? l - nwin : l;
+                j = wrap ? j + 1 : j;
+            }
+            const bool real = j < nuw;
+            l = real ? l : nwin - 1;
+            const int unit = real ? u_first + w + 4 * j : last_unit;
+            const int want = 8 * l;
+            const int got = min(want, sbytes - 8);
+            ssh0[d / kGroup] = ssh1[d / kGroup] = (want - got) >> 2;
+            sv0[d / kGroup] = moe::gload<u32x2_t>(sbase0 + (size_t)unit * sustride + got);
+            sv1[d / kGroup] = moe::gload<u32x2_t>(sbase1 + (size_t)unit * sustride + got);
+        }
+        const bool real = lj < nuw;  // past the end: the last real step again
+        const int unit = real ? u_first + w + 4 * lj : last_unit;
+        const int off = min(64 * (real ? lw : nwin - 1) + 16 * q, rowbytes - 16);
+        w0[d] = moe::gload<u32x4_t>(wb0 + (size_t)unit * ustride + off);
+        w1[d] = moe::gload<u32x4_t>(wb1 + (size_t)unit * ustride + off);
+        if (++lw == nwin) {
+            lw = 0;
+            ++lj;
+        }
+    };
+
+    if (threadIdx.x < 16) rmax[threadIdx.x] = 0u;
+    const bool x_first = !GATED || a.single_token;
+    int tokv = 0;
+    if (!x_first) {
+        if constexpr (TOK_LDS)
+            tokv = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[row0 + min(lane & 15, pr - 1)];
+        else
+            tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    }
+    __syncthreads();  // rmax cleared
+    __builtin_amdgcn_sched_barrier(0);
+    if (x_first) {
+        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                load(d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    } else {
+        load(0);
+        __builtin_amdgcn_sched_barrier(0);
+        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 1; d < D; ++d) {
+                load(d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    }
+
+    // A operand: row n of the pass (rows past it read row 0: dropped outputs).
+    const int arow = (n < pr ? n : 0) * ldx;
+    float oscale[4];  // undoes the row scaling of this lane's output rows 4 q + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = 4 * q + v;
+        oscale[v] = exp2i(row_exp(rmax[t < pr ? t : 0]));
+    }
+    // This lane's scale bytes in a step's slice: group g at 128 g + 8 n + 2 q.
+    const int sread = 8 * n + 2 * q;
+
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    int cj = 0, cw = 0;  // stream position being computed
+    auto step = [&](const int d, auto refill) {
+        if (d % kGroup == 0) {
+            // This group's scales -> LDS at [step s4][group sg][row][8 bytes].
+            const int sh = ssh0[d / kGroup];
+            const u32x2_t v0 = sv0[d / kGroup], v1 = sv1[d / kGroup];
+            const u32x2_t r0 = {sh == 0 ? v0[0] : v0[1], v0[1]};
+            const u32x2_t r1 = {sh == 0 ? v1[0] : v1[1], v1[1]};
+            *reinterpret_cast<u32x2_t *>(sc_lds + 256 * s4 + 128 * sg + 8 * n8) = r0;
+            *reinterpret_cast<u32x2_t *>(sc_lds + 256 * s4 + 128 * sg + 8 * (n8 + 8)) = r1;
+        }
+        const int k0 = 128 * cw + 32 * q;  // first k of this lane's chunk
+        const bool kin = cj < nuw && k0 < K;
+        const int kac = k0 < K ? k0 : 0;   // past the end: any finite row data
+        f16x8_t av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const f16x8_t *>(xs + arow + kac + 8 * i);
+        const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread;
+        const uint32_t u0 = *reinterpret_cast<const uint16_t *>(sp);
+        const uint32_t u1 = *reinterpret_cast<const uint16_t *>(sp + 128);
+        const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
+        const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u0, 1.0f, false) : zero2;
+        const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u1, 1.0f, false) : zero2;
+        const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
+        const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x8_t b0 = decode_b(w0[d][i], i < 2 ? sl0 : sh0);
+            const f16x8_t b1 = decode_b(w1[d][i], i < 2 ? sl1 : sh1);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], b1, acc1, 0, 0, 0);
+        }
+        if (cj < nuw && cw == nwin - 1) {  // uniform: this unit is complete
+            const int unit = u_first + w + 4 * cj;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = 4 * q + v;  // C row (pass row) of acc*[v]; column n
+                if (t < pr) {
+                    float *o = a.out + (size_t)(row0 + t) * N;
+                    if constexpr (GATED) {
+                        o[16 * unit + n] = moe::silu_f32(acc0[v] * oscale[v] * s2A) * (acc1[v] * oscale[v] * s2B);
+                    } else {
+                        o[32 * unit + n] = acc0[v] * oscale[v] * s2A;
+                        o[32 * unit + 16 + n] = acc1[v] * oscale[v] * s2A;
+                    }
+                }
+            }
+            acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (++cw == nwin) {
+            cw = 0;
+            ++cj;
+        }
+        if constexpr (decltype(refill)::value) {
+            __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
+            load(d);
+            __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
+        }
+    };
+    int base = 0;
+    for (; base + D < total; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) step(d, std::true_type{});
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(d, std::false_type{});
+}
+
 // Passes beyond the first of an expert with r routed rows.
 __device__ __forceinline__ int further_passes(int r, int pr) { return r <= 0 ? 0 : (r - 1) / pr; }
 
@@ -629,7 +830,15 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
         }
         return;
     }
-    run_pass<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+    // Passes of more than 8 rows run token-dense: one MFMA per 16 rows instead
+    // of one per 4.  (At 5..8 rows the saving is smaller than the cost of the
+    // dense pass's coarser split, a whole unit per wave, which leaves waves
+    // idle when a block holds few units: 64 tokens x 256 experts ran 11%
+    // slower with the threshold at 4.)
+    if (pr > 8)
+        run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+    else
+        run_pass<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
 }
 
 template <bool GATED>

@@ -259,14 +259,15 @@ def test_kmajor_matches_rowmajor_on_same_weights():
     parity.assert_parity(ob, ref["out"], "K-major")
 
 
-@pytest.mark.parametrize("kmajor", [False, True])
-def test_activation_range(kmajor):
+@pytest.mark.parametrize("kmajor,T,E", [(False, 6, 4), (True, 6, 4), (False, 40, 2)])
+def test_activation_range(kmajor, T, E):
     """Token rows scaled by 2^40, 2^-40 and 2^60 (beyond fp16's range either
     way): the decode path stages each row with its own power-of-two factor and
     the many-token path computes in bf16, so every row of h, y and out follows
-    the oracle at its own magnitude (scale-invariant rules, row by row)."""
-    say("activation range", "kmajor" if kmajor else "row-major")
-    shape = synth.MoeShape("range", 6, 512, 384, 4, 2, "uniform", kmajor)
+    the oracle at its own magnitude (scale-invariant rules, row by row).
+    40 tokens over 2 experts puts the decode passes on the token-dense path."""
+    say("activation range", "kmajor" if kmajor else "row-major", T, E)
+    shape = synth.MoeShape("range", T, 512, 384, E, 2, "uniform", kmajor)
     case = Case(16, shape)
     bits = case.x_bits.astype(np.uint32)
     shift = {1: 40, 2: -40, 4: 60}  # h of the 2^60 row is near 2^108, inside fp32
