@@ -555,7 +555,7 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
     for (int d = 0; d < D; ++d) step(d, std::false_type{});
 }
 
-// Token-dense pass, for passes of more than 8 rows.  The (row, quarter)
+// Token-dense pass, for passes of more than 4 rows.  The (row, quarter)
 // layout above feeds 4 tokens per MFMA and keeps a quarter of each result,
 // so a pass of 16 rows costs 4 MFMAs per decoded operand; here one MFMA
 // takes all 16 rows of the pass.  Each B column is one weight row: lane
@@ -565,13 +565,14 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
 // lane, i.e. k = 128 window + 32 q + 8 d + i in B slot (q, i); the A operand
 // (x rows of the pass, staged as above) is read at the same k.  The k order
 // inside the sum differs from the plain order; the products do not.
-//   * A wave owns whole units (gate+up: the 16 gate and 16 up rows of 16
-//     output columns; down: 32 output rows as two groups of 16), taking the
-//     block's units round-robin; a step is one 64-byte window of its two
-//     16-row groups.
-//   * Scales: every 4 steps each lane loads the 8 scale bytes of one (step,
-//     group, row) into the wave's 1 KiB LDS area; a step reads its two bytes
-//     per lane from there.
+//   * Work items of 16 weight rows, two per unit, taken round-robin by the
+//     waves: gate+up, 8 gate rows and the 8 up rows of the same 8 output
+//     columns (lane n and lane n + 8 meet through a lane swap for the SiLU
+//     product); down, 16 output rows.  A step is two 64-byte windows of the
+//     item's rows.
+//   * Scales: every 4 steps each lane loads 16 scale bytes (one row, one
+//     step: two windows) into the wave's 1 KiB LDS area; a step reads its
+//     two bytes per window per lane from there.
 template <bool GATED, int D, bool TOK_LDS>
 __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                                const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
@@ -580,64 +581,61 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
     const int K = a.K, N = a.N, ldx = a.ldx;
     const int rowbytes = K >> 1, sbytes = K >> 4;
     const int nwin = (rowbytes + 63) >> 6;  // 64-byte windows (128 k) per row
+    const int nstep = (nwin + 1) >> 1;      // two windows per step
     const int lane = threadIdx.x & 63, w = moe::wave_id();
     const int n = lane & 15, q = lane >> 4;
-    const int nuw = nu > w ? (nu - w + 3) >> 2 : 0;  // units of this wave: u_first + w + 4 j
-    const int total = nuw * nwin;
-    // Unit read past the end of this wave's list (a wave with none reads the
-    // block's first unit): the addresses stay inside the expert's weights.
-    const int last_unit = nuw > 0 ? u_first + w + 4 * (nuw - 1) : u_first;
-    // Scale-load role: step s4 of the group, row n of group sg.
-    const int s4 = lane >> 4, sg = (lane >> 3) & 1;
-    // (lanes 0..63 cover 4 steps x 2 groups x 8 rows per load; two loads per
-    //  group cover the 16 rows: row n8 + 8 h)
-    const int n8 = lane & 7;
+    const int i_first = 2 * u_first, nit = 2 * nu;  // items of the block
+    const int niw = nit > w ? (nit - w + 3) >> 2 : 0;  // items of this wave: i_first + w + 4 j
+    const int total = niw * nstep;
+    // Item read past the end of this wave's list (a wave with none reads the
+    // block's first item): the addresses stay inside the expert's weights.
+    const int last_item = niw > 0 ? i_first + w + 4 * (niw - 1) : i_first;
 
     uint8_t *sc_lds = lds + w * kScaleLds;
     uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kRmaxOff);
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds + kHdrLds);
 
-    // Row bases of this lane's two weight rows in unit 0, and the unit stride.
-    const uint8_t *wb0 = pA + (size_t)n * rowbytes;
-    const uint8_t *wb1 = GATED ? pB + (size_t)n * rowbytes : pA + (size_t)(16 + n) * rowbytes;
-    const size_t ustride = (size_t)(GATED ? 16 : 32) * rowbytes;
-    // Scale rows loaded by this lane (rows n8 and n8 + 8 of group sg), unit 0.
-    const uint8_t *sgb = sg == 0 ? sA : (GATED ? sB : sA);
-    const int sgrow0 = (GATED || sg == 0) ? 0 : 16;
-    const uint8_t *sbase0 = sgb + (size_t)(sgrow0 + n8) * sbytes;
-    const uint8_t *sbase1 = sgb + (size_t)(sgrow0 + n8 + 8) * sbytes;
-    const size_t sustride = (size_t)(GATED ? 16 : 32) * sbytes;
+    // Weight row of lane n in item 0, and the item stride (rows).
+    //   gate+up: rows 8 i + n of gate (n < 8) or 8 i + n - 8 of up;
+    //   down:    rows 16 i + n.
+    const bool upl = GATED && n >= 8;
+    const uint8_t *wb = (upl ? pB : pA) + (size_t)(GATED ? (n & 7) : n) * rowbytes;
+    const size_t istride = (size_t)(GATED ? 8 : 16) * rowbytes;
+    // Scale role: row r = lane >> 2 of the item, step s4 = lane & 3 of the group.
+    const int r = lane >> 2, s4 = lane & 3;
+    const bool upr = GATED && r >= 8;
+    const uint8_t *sb = (upr ? sB : sA) + (size_t)(GATED ? (r & 7) : r) * sbytes;
+    const size_t sistride = (size_t)(GATED ? 8 : 16) * sbytes;
 
-    u32x4_t w0[D], w1[D];
-    u32x2_t sv0[D / kGroup], sv1[D / kGroup];
-    int ssh0[D / kGroup], ssh1[D / kGroup];  // dword shift of a clamped scale load
-    int lj = 0, lw = 0;                      // stream position of the next load (unit, window)
+    u32x4_t w0[D], w1[D], sv[D / kGroup];
+    int ssh[D / kGroup];  // dword shift of a clamped scale load
+    int lj = 0, ls = 0;   // stream position of the next load (item, step)
     auto load = [&](int d) {
         if (d % kGroup == 0) {
-            // Scales of step (lj, lw) + s4: 8 bytes of window l for rows n8, n8 + 8 of group sg.
-            int l = lw + s4, j = lj;
+            // Scales of step (lj, ls) + s4 for row r: 16 bytes at 16 step.
+            int l = ls + s4, j = lj;
 #pragma unroll
             for (int i = 0; i < kGroup - 1; ++i) {
-                const bool wrap = l >= nwin;
-                l = wrap ? l - nwin : l;
+                const bool wrap = l >= nstep;
+                l = wrap ? l - nstep : l;
                 j = wrap ? j + 1 : j;
             }
-            const bool real = j < nuw;
-            l = real ? l : nwin - 1;
-            const int unit = real ? u_first + w + 4 * j : last_unit;
-            const int want = 8 * l;
-            const int got = min(want, sbytes - 8);
-            ssh0[d / kGroup] = ssh1[d / kGroup] = (want - got) >> 2;
-            sv0[d / kGroup] = moe::gload<u32x2_t>(sbase0 + (size_t)unit * sustride + got);
-            sv1[d / kGroup] = moe::gload<u32x2_t>(sbase1 + (size_t)unit * sustride + got);
+            const bool real = j < niw;
+            const int item = real ? i_first + w + 4 * j : last_item;
+            l = real ? l : nstep - 1;
+            const int want = 16 * l;
+            const int got = min(want, sbytes - 16);
+            ssh[d / kGroup] = (want - got) >> 2;
+            sv[d / kGroup] = moe::gload<u32x4_t>(sb + (size_t)item * sistride + got);
         }
-        const bool real = lj < nuw;  // past the end: the last real step again
-        const int unit = real ? u_first + w + 4 * lj : last_unit;
-        const int off = min(64 * (real ? lw : nwin - 1) + 16 * q, rowbytes - 16);
-        w0[d] = moe::gload<u32x4_t>(wb0 + (size_t)unit * ustride + off);
-        w1[d] = moe::gload<u32x4_t>(wb1 + (size_t)unit * ustride + off);
-        if (++lw == nwin) {
-            lw = 0;
+        const bool real = lj < niw;  // past the end: the last real step again
+        const int item = real ? i_first + w + 4 * lj : last_item;
+        const int st = real ? ls : nstep - 1;
+        const uint8_t *rb = wb + (size_t)item * istride;
+        w0[d] = moe::gload<u32x4_t>(rb + min(128 * st + 16 * q, rowbytes - 16));
+        w1[d] = moe::gload<u32x4_t>(rb + min(128 * st + 64 + 16 * q, rowbytes - 16));
+        if (++ls == nstep) {
+            ls = 0;
             ++lj;
         }
     };
@@ -683,61 +681,58 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
         const int t = 4 * q + v;
         oscale[v] = exp2i(row_exp(rmax[t < pr ? t : 0]));
     }
-    // This lane's scale bytes in a step's slice: group g at 128 g + 8 n + 2 q.
-    const int sread = 8 * n + 2 * q;
+    const float s2l = upl ? s2B : s2A;  // scale_2 of this lane's weight row
 
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    int cj = 0, cw = 0;  // stream position being computed
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int cj = 0, cs = 0;  // stream position being computed
     auto step = [&](const int d, auto refill) {
         if (d % kGroup == 0) {
-            // This group's scales -> LDS at [step s4][group sg][row][8 bytes].
-            const int sh = ssh0[d / kGroup];
-            const u32x2_t v0 = sv0[d / kGroup], v1 = sv1[d / kGroup];
-            const u32x2_t r0 = {sh == 0 ? v0[0] : v0[1], v0[1]};
-            const u32x2_t r1 = {sh == 0 ? v1[0] : v1[1], v1[1]};
-            *reinterpret_cast<u32x2_t *>(sc_lds + 256 * s4 + 128 * sg + 8 * n8) = r0;
-            *reinterpret_cast<u32x2_t *>(sc_lds + 256 * s4 + 128 * sg + 8 * (n8 + 8)) = r1;
+            // This group's scales -> LDS at [step s4][row r][16 bytes] (undoing a clamped load's shift).
+            const u32x4_t v = sv[d / kGroup];
+            const int sh = ssh[d / kGroup];
+            u32x4_t t;
+            t[0] = sh == 0 ? v[0] : (sh == 1 ? v[1] : (sh == 2 ? v[2] : v[3]));
+            t[1] = sh == 0 ? v[1] : (sh == 1 ? v[2] : v[3]);
+            t[2] = sh == 0 ? v[2] : v[3];
+            t[3] = v[3];
+            *reinterpret_cast<u32x4_t *>(sc_lds + 256 * s4 + 16 * r) = t;
         }
-        const int k0 = 128 * cw + 32 * q;  // first k of this lane's chunk
-        const bool kin = cj < nuw && k0 < K;
-        const int kac = k0 < K ? k0 : 0;   // past the end: any finite row data
-        f16x8_t av[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const f16x8_t *>(xs + arow + kac + 8 * i);
-        const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread;
-        const uint32_t u0 = *reinterpret_cast<const uint16_t *>(sp);
-        const uint32_t u1 = *reinterpret_cast<const uint16_t *>(sp + 128);
+        const uint8_t *sp = sc_lds + 256 * (d % kGroup) + 16 * n + 2 * q;
+        const uint32_t u0 = *reinterpret_cast<const uint16_t *>(sp);      // window 2 step
+        const uint32_t u1 = *reinterpret_cast<const uint16_t *>(sp + 8);  // window 2 step + 1
         const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
-        const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u0, 1.0f, false) : zero2;
-        const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u1, 1.0f, false) : zero2;
-        const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
-        const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f16x8_t b0 = decode_b(w0[d][i], i < 2 ? sl0 : sh0);
-            const f16x8_t b1 = decode_b(w1[d][i], i < 2 ? sl1 : sh1);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], b1, acc1, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+            const int k0 = 128 * (2 * cs + h) + 32 * q;  // first k of this lane's chunk
+            const bool kin = cj < niw && k0 < K;
+            const int kac = k0 < K ? k0 : 0;  // past the end: any finite row data
+            const f16x2_t sf = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h ? u1 : u0, 1.0f, false) : zero2;
+            const f16x2_t sl = {sf.x, sf.x}, sh = {sf.y, sf.y};
+            const u32x4_t wv = h ? w1[d] : w0[d];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f16x8_t av = *reinterpret_cast<const f16x8_t *>(xs + arow + kac + 8 * i);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_b(wv[i], i < 2 ? sl : sh), acc, 0, 0, 0);
+            }
         }
-        if (cj < nuw && cw == nwin - 1) {  // uniform: this unit is complete
-            const int unit = u_first + w + 4 * cj;
+        if (cj < niw && cs == nstep - 1) {  // uniform: this item is complete
+            const int item = i_first + w + 4 * cj;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 4 * q + v;  // C row (pass row) of acc*[v]; column n
-                if (t < pr) {
-                    float *o = a.out + (size_t)(row0 + t) * N;
-                    if constexpr (GATED) {
-                        o[16 * unit + n] = moe::silu_f32(acc0[v] * oscale[v] * s2A) * (acc1[v] * oscale[v] * s2B);
-                    } else {
-                        o[32 * unit + n] = acc0[v] * oscale[v] * s2A;
-                        o[32 * unit + 16 + n] = acc1[v] * oscale[v] * s2A;
-                    }
+                const int t = 4 * q + v;  // C row (pass row) of acc[v]; column n
+                const float val = acc[v] * oscale[v] * s2l;
+                if constexpr (GATED) {
+                    const float other = __shfl_xor(val, 8, 16);  // lane n <-> n + 8: gate <-> up
+                    if (t < pr && !upl)
+                        a.out[(size_t)(row0 + t) * N + 8 * item + n] = moe::silu_f32(val) * other;
+                } else {
+                    if (t < pr) a.out[(size_t)(row0 + t) * N + 16 * item + n] = val;
                 }
             }
-            acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if (++cw == nwin) {
-            cw = 0;
+        if (++cs == nstep) {
+            cs = 0;
             ++cj;
         }
         if constexpr (decltype(refill)::value) {
@@ -834,12 +829,9 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
         }
         return;
     }
-    // Passes of more than 8 rows run token-dense: one MFMA per 16 rows instead
-    // of one per 4.  (At 5..8 rows the saving is smaller than the cost of the
-    // dense pass's coarser split, a whole unit per wave, which leaves waves
-    // idle when a block holds few units: 64 tokens x 256 experts ran 11%
-    // slower with the threshold at 4.)
-    if (pr > 8)
+    // Passes of more than 4 rows (more than one token group) run token-dense:
+    // one MFMA per 16 rows instead of one per 4.
+    if (pr > 4)
         run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
     else
         run_pass<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
