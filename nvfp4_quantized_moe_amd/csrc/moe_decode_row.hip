@@ -43,7 +43,7 @@
 //     (exact: at most 6 significant bits, range 2^-10 .. 2688).  A pass
 //     handles up to 16 routed rows (4 MFMA token groups) sharing each decoded
 //     weight; experts with more rows than the staged activation holds take
-//     further passes.  Passes of more than 8 rows take the token-dense form
+//     further passes.  Passes of more than 4 rows take the token-dense form
 //     (run_pass_dense): 16 rows x 64 bytes per load, one weight row per B
 //     column, all 16 rows of the pass in one MFMA.
 //   * Routing sort fused in (k_decode_row<true, true>): with few pairs, every
