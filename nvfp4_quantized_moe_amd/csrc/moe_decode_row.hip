@@ -1045,8 +1045,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     const int n = *a.nactive;
     cost_prefix(a, n, pre);
     const int total = pre[n];
-    const int c0 = (int)((int64_t)total * blockIdx.x / gridDim.x);
-    const int c1 = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+    // Blocks go to the 8 XCDs round-robin; consecutive shares go to one XCD,
+    // so the later passes of an expert mostly run where its earlier passes
+    // left the weights in L2.
+    const int g = gridDim.x;
+    const int bx = (g & 7) == 0 ? (int)((blockIdx.x & 7) * (g >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+    const int c0 = (int)((int64_t)total * bx / g);
+    const int c1 = (int)((int64_t)total * (bx + 1) / g);
     Cursor k = locate(a, pre, n, c0);
     const Cursor end = locate(a, pre, n, c1);
     bool first = true;
