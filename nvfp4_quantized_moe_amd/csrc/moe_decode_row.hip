@@ -40,12 +40,12 @@
 //     the blocks where the two quarters agree are kept, and the 4 quarters are
 //     summed across a quad of lanes at the end of the unit.  The E2M1 codes
 //     are widened to fp16 pairs and multiplied by the E4M3 scale in fp16
-//     (exact: at most 6 significant bits, range 2^-10 .. 2688).  A pass
-//     handles up to 16 routed rows (4 MFMA token groups) sharing each decoded
-//     weight; experts with more rows than the staged activation holds take
-//     further passes.  Passes of more than 4 rows take the token-dense form
-//     (run_pass_dense): 16 rows x 64 bytes per load, one weight row per B
-//     column, all 16 rows of the pass in one MFMA.
+//     (exact: at most 6 significant bits, range 2^-10 .. 2688).  This layout
+//     serves passes of up to 4 routed rows (one MFMA token group); longer
+//     passes, up to 16 rows sharing each decoded weight, take the
+//     token-dense form (run_pass_dense): 16 rows x 64 bytes per load, one
+//     weight row per B column, all 16 rows of the pass in one MFMA.  Experts
+//     with more rows than the staged activation holds take further passes.
 //   * Routing sort fused in (k_decode_row<true, true>): with few pairs, every
 //     wave ranks them itself and block (0, 0) writes the sort outputs.
 //   * Activations.  LDS holds the pass's activation rows (x rows for gate+up,
@@ -66,7 +66,7 @@ constexpr int kWaves = kThreads / moe::kWave;
 constexpr int kDepth = 4;          // ring: steps in flight per wave (a multiple of kGroup)
 constexpr int kGroup = 4;          // steps per scale load
 constexpr int kSegBytes = 256;     // bytes of one weight row per step (512 k)
-constexpr int kMaxTG = 4;          // token groups of 4 per pass (16 rows)
+constexpr int kMaxTG = 4;          // token groups of 4 per pass (16 rows, token-dense above 4)
 constexpr int kLdsBudget = 72 * 1024;  // staged activation rows per block (two blocks per CU)
 constexpr int kScaleLds = 1024;        // per wave: 4 steps x 8 rows x 32 bytes
 constexpr int kPreLds = 4 * (MOE_NVFP4_MAX_EXPERTS + 4);  // per-slot prefix sums of passes (or the fused sort)
@@ -330,6 +330,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
 
 // One pass: rows [row0, row0 + pr) of the expert against units
 // [u_first, u_first + nu) of its weights.
+// A pass of up to 4 rows in the (row, quarter) layout.
 template <bool GATED, int D, bool TOK_LDS>  // TOK_LDS: pass tokens from the fused sort's LDS table
 __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                          const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
@@ -438,22 +439,14 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
         });
     }
 
-    const int TG = (pr + 3) >> 2;
-    const int tA = n >> 2, cA = n & 3;  // A-operand role: token tA of each group, quarter cA
-    int arow[kMaxTG];
-    float oscale[kMaxTG];  // undoes the row scaling of this lane's output token
-#pragma unroll
-    for (int tg = 0; tg < kMaxTG; ++tg) {
-        const int t = 4 * tg + tA;
-        arow[tg] = (t < pr ? t : 0) * ldx;  // rows past the pass read row 0: dropped outputs
-        const int to = 4 * tg + q;
-        oscale[tg] = exp2i(row_exp(rmax[to < pr ? to : 0]));
-    }
+    // One token group (pr <= 4): lane (n, q) feeds A row (token n >> 2,
+    // quarter n & 3) and its output row is token q.
+    const int tA = n >> 2, cA = n & 3;
+    const int arow = (tA < pr ? tA : 0) * ldx;  // rows past the pass read row 0: dropped outputs
+    const float oscale = exp2i(row_exp(rmax[q < pr ? q : 0]));  // undoes the row scaling of token q
     const int sread0 = 32 * rho + 8 * q + 2 * c;  // this lane's scale bytes in a step's slice (group 0)
 
-    f32x4_t acc0[kMaxTG], acc1[kMaxTG];
-#pragma unroll
-    for (int tg = 0; tg < kMaxTG; ++tg) acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 
     int cu = 0, ci = 0;  // stream position being computed
     // One step of the ring: compute slot d, then (refill) load the step D
@@ -472,13 +465,12 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
             r[3] = v[3];
             *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
         }
-        // A fragments of token group 0 (always present), read first so the
-        // LDS latency hides behind the decode.
+        // A fragments, read first so the LDS latency hides behind the decode.
         const int ka = 512 * ci + 128 * q + 32 * cA;  // first k of this lane's A fragment
         const int kac = ka < K ? ka : 0;              // past the end: any finite row data
         f16x8_t a0[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + arow[0] + kac + 8 * ks);
+        for (int ks = 0; ks < 4; ++ks) a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + arow + kac + 8 * ks);
         const int kq = 512 * ci + 128 * q + 32 * c;  // first k of this lane's B chunk
         const bool kin = cu < nu && kq < K;
         const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
@@ -497,43 +489,25 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            acc0[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0[0], 0, 0, 0);
-            acc1[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1[0], 0, 0, 0);
-        }
-#pragma unroll
-        for (int tg = 1; tg < kMaxTG; ++tg) {
-            if (tg < TG) {
-                const uint16_t *ap = xs + arow[tg] + kac;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const f16x8_t A = *reinterpret_cast<const f16x8_t *>(ap + 8 * ks);
-                    acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b0[ks], acc0[tg], 0, 0, 0);
-                    acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b1[ks], acc1[tg], 0, 0, 0);
-                }
-            }
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1, 0, 0, 0);
         }
         if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
             const int unit = u_first + cu;
-#pragma unroll
-            for (int tg = 0; tg < kMaxTG; ++tg) {
-                if (tg < TG) {
-                    // Lane (n, t) holds rows 4t..4t+3 of column n; the kept
-                    // block is row 4t + (n & 3).  Sum the quarters of a quad.
-                    const float g0 = moe::group_sum<4>(pick(acc0[tg], c)) * oscale[tg];
-                    const float g1 = moe::group_sum<4>(pick(acc1[tg], c)) * oscale[tg];
-                    const int tl = 4 * tg + q;
-                    if (c == 0 && tl < pr) {
-                        float *o = a.out + (size_t)(row0 + tl) * N;
-                        if constexpr (GATED) {
-                            o[16 * unit + 4 * w + rho] = moe::silu_f32(g0 * s2A) * (g1 * s2B);
-                        } else {
-                            o[32 * unit + 8 * w + rho] = g0 * s2A;
-                            o[32 * unit + 8 * w + 4 + rho] = g1 * s2A;
-                        }
-                    }
-                    acc0[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // Lane (n, q) holds rows 4q..4q+3 of column n; the kept block is
+            // row 4q + (n & 3), i.e. token q.  Sum the quarters of a quad.
+            const float g0 = moe::group_sum<4>(pick(acc0, c)) * oscale;
+            const float g1 = moe::group_sum<4>(pick(acc1, c)) * oscale;
+            if (c == 0 && q < pr) {
+                float *o = a.out + (size_t)(row0 + q) * N;
+                if constexpr (GATED) {
+                    o[16 * unit + 4 * w + rho] = moe::silu_f32(g0 * s2A) * (g1 * s2B);
+                } else {
+                    o[32 * unit + 8 * w + rho] = g0 * s2A;
+                    o[32 * unit + 8 * w + 4 + rho] = g1 * s2A;
                 }
             }
+            acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         if (++ci == nseg) {
             ci = 0;
