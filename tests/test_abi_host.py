@@ -148,3 +148,15 @@ def test_sort_gate_up_launch_count_query():
     assert L.moe_nvfp4_sort_gate_up_launches(2048, 4, 64, 4096, 1536, 1) == 2
     assert L.moe_nvfp4_sort_gate_up_launches(4, 2, 4, 256, 512, 7) == ELAYOUT
     assert L.moe_nvfp4_sort_gate_up_launches(4, 5, 4, 256, 512, 0) == ESHAPE
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No CPU fallback: with the HIP library absent every entry point raises."""
+    import torch
+
+    monkeypatch.setattr(moe, "LIB_PATH", tmp_path / "libmoe_nvfp4.so")
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.transpose_u8(torch.zeros(4, dtype=torch.uint8), torch.zeros(4, dtype=torch.uint8), 2, 2)
