@@ -10,7 +10,16 @@
  *   moe_nvfp4_blend         out[t] = sum_j w[t, j] * y[pair of (t, j)]
  *
  * plus a load-time byte transpose, transpose_u8, that builds the K-major
- * transposed twin of a weight for the many-token path.
+ * transposed twin of a weight for the many-token path.  Also declared here:
+ *
+ *   moe_nvfp4_route                 the router ahead of the path (softmax,
+ *                                   top-k, weights renormalised over the k)
+ *   moe_nvfp4_sort_gate_up_silu     sort + gate+up, one launch at few pairs
+ *   moe_nvfp4_sort_gate_up_launches host-only: is that one launch or two
+ *   transpose_u8_pitched,           a concatenated gate||up K-major twin with
+ *   moe_nvfp4_gate_up_silu_concat   a padded row pitch, and gate+up over it
+ *
+ * and the layout MOE_NVFP4_K_MAJOR_MXFP4 (MXFP4 experts: E8M0 scales per 32).
  *
  * Sources of the operations (the reference pages are Rust source pages of a
  * model runtime; each is cited by its file name and the item on it):
@@ -36,7 +45,8 @@
  *     was launched; a positive hipError_t if a launch itself failed.
  *   - Shapes: T tokens, k experts per token (top-k), P = T * k routed pairs,
  *     E experts, H hidden width, I expert intermediate width.  Matrices are
- *     row-major and dense (row stride = row length).
+ *     row-major and dense (row stride = row length), except the
+ *     concatenated twin, whose row pitch is an argument.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  */
 #ifndef MOE_NVFP4_H
