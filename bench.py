@@ -4,8 +4,9 @@
                     [--gate-up separate|concat]
 
 A step is one MoE layer forward through the whole path — routing sort,
-gate+up+SiLU, down, blend — over one batch of synthetic input (at a few
-tokens the sort runs inside the gate+up launch).  Every input
+gate+up+SiLU, down, blend — over one batch of synthetic input (at one
+token the sort runs inside the gate+up launch and the blend inside the down
+launch).  Every input
 is resident in HBM before timing starts.  Consecutive steps run different
 layers' expert weights (separate HBM copies, as successive layers of a model
 would), so the weights a step reads were last touched far more than the

@@ -16,6 +16,7 @@
  *                                   top-k, weights renormalised over the k)
  *   moe_nvfp4_sort_gate_up_silu     sort + gate+up, one launch at few pairs
  *   moe_nvfp4_sort_gate_up_launches host-only: is that one launch or two
+ *   moe_nvfp4_down_blend            down + blend in one launch (few tokens)
  *   transpose_u8_pitched,           a concatenated gate||up K-major twin with
  *   moe_nvfp4_gate_up_silu_concat   a padded row pitch, and gate+up over it
  *
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 5
+#define MOE_NVFP4_ABI_VERSION 6
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
 #define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
@@ -260,6 +261,38 @@ int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, i
  */
 int moe_nvfp4_blend(const float *y, const float *topk_weights, const int32_t *pair_pos,
                     int32_t T, int32_t k, int32_t H, uint16_t *out, void *stream);
+
+/*
+ * moe_nvfp4_down_blend — moe_nvfp4_down followed by moe_nvfp4_blend, in one
+ * launch and without the y tensor (nvfp4_moe_grouped.rs, module doc: the
+ * down projection of every routed pair, then the weighted sum of each
+ * token's rows):
+ *     out[t, n] = bf16_rne( sum_{j=0..k-1} topk_weights[t, j] * y_j[n] ),
+ *     y_j[n]    = sum_i h[p, i] * Wd_e[n, i],  p = pair_pos[t*k+j], e = topk_ids[t*k+j],
+ * summed in fp32 in ascending j; a pair with pair_pos < 0 adds nothing and a
+ * pair whose expert is NULL adds w * 0.  Each y value is the one
+ * moe_nvfp4_down computes, so out equals moe_nvfp4_down then
+ * moe_nvfp4_blend bit for bit while no expert holds more than 4 routed pairs
+ * (so for one token unless an id repeats more than 4 times; beyond that the
+ * two differ only in the order of the fp32 sums inside a dot product).  One
+ * block serves
+ * one token for all of its pairs, so an expert's weights are read once per
+ * token routed to it: meant for decode with one or a few tokens.
+ *
+ *   h             in  fp32 [P, I] (moe_nvfp4_gate_up_silu's output)
+ *   down          NVFP4 table, ROW_MAJOR only; N = H, K = I.
+ *   topk_ids      in  int32 [T, k] (the ids given to moe_nvfp4_sort)
+ *   topk_weights  in  fp32 [T, k]
+ *   pair_pos      in  int32 [T*k]  (moe_nvfp4_sort's output)
+ *   out           out bf16 [T, H]
+ * Admission: as moe_nvfp4_down for ROW_MAJOR, plus k <= 64, T <= 65535 and
+ * the token's k activation rows staged in shared memory:
+ * k * (2 I + pad) <= 73728 bytes (pad < 256), ELIMIT above.
+ * Errors: ENULL, ESHAPE, ELAYOUT (any layout but ROW_MAJOR), ELIMIT.
+ */
+int moe_nvfp4_down_blend(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                         moe_nvfp4_experts down, const int32_t *topk_ids, const float *topk_weights,
+                         const int32_t *pair_pos, uint16_t *out, void *stream);
 
 /*
  * transpose_u8 — out-of-place byte-matrix transpose

@@ -36,6 +36,7 @@ __all__ = [
     "moe_nvfp4_gate_up_silu",
     "moe_nvfp4_down",
     "moe_nvfp4_blend",
+    "moe_nvfp4_down_blend",
     "transpose_u8",
     "transpose_u8_pitched",
     "transpose_for_gemm",
@@ -57,6 +58,7 @@ LIB_PATH = _PKG / "libmoe_nvfp4.so"
 HEADER = _PKG.parent / "include" / "moe_nvfp4.h"
 
 _ERRNAMES = {-1: "ENULL", -2: "ESHAPE", -3: "ELAYOUT", -4: "ELIMIT"}
+_ELIMIT = -4
 
 
 class MoeNvfp4Error(RuntimeError):
@@ -100,10 +102,11 @@ def lib() -> ctypes.CDLL:
         L.moe_nvfp4_sort_gate_up_silu.argtypes = [_P, _P, _I, _I, _I, _I, _I, _Experts, _Experts, _P, _P, _P, _P,
                                                   _P, _P, _P, _P]
         L.moe_nvfp4_sort_gate_up_launches.argtypes = [_I, _I, _I, _I, _I, _I]
+        L.moe_nvfp4_down_blend.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _P, _P, _P, _P, _P]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                    "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version", "transpose_u8_pitched",
                    "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
-                   "moe_nvfp4_sort_gate_up_launches"):
+                   "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,6 +269,23 @@ def moe_nvfp4_blend(y, topk_weights, pair_pos, out, stream=None) -> None:
     _check("moe_nvfp4_blend", rc)
 
 
+def _down_blend_rc(h, topk_ids, topk_weights, pair_pos, E, H, I, down: ExpertTables, out, stream) -> int:
+    T, k = topk_weights.shape
+    return lib().moe_nvfp4_down_blend(
+        _dev(h, torch.float32, "h"), T, k, E, H, I, down.abi(),
+        _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights"),
+        _dev(pair_pos, torch.int32, "pair_pos"),
+        _dev(out, torch.bfloat16, "out") if out.dtype == torch.bfloat16 else _dev(out, torch.int16, "out"),
+        _stream(stream))
+
+
+def moe_nvfp4_down_blend(h, topk_ids, topk_weights, pair_pos, E, H, I, down: ExpertTables, out,
+                         stream=None) -> None:
+    """Down projection and top-k blend in one launch (row-major weights; meant
+    for decode with one or a few tokens)."""
+    _check("moe_nvfp4_down_blend", _down_blend_rc(h, topk_ids, topk_weights, pair_pos, E, H, I, down, out, stream))
+
+
 def transpose_u8(src, dst, rows, cols, stream=None) -> None:
     if src.numel() != rows * cols or dst.numel() != rows * cols:
         raise ValueError("transpose_u8: tensor sizes do not match rows * cols")
@@ -358,8 +378,9 @@ class MoeLayer:
 
     ``gate``, ``up`` and ``down`` are ExpertTables (the same layout for all
     three).  ``forward`` enqueues sort -> gate_up_silu -> down -> blend on
-    the current stream and returns the bf16 output [T, H]; the intermediate
-    buffers stay available as attributes for inspection.
+    the current stream (with sort and gate+up, or down and blend, fused into
+    one launch where that pays) and returns the bf16 output [T, H]; the
+    intermediate buffers stay available as attributes for inspection.
     """
 
     def __init__(self, T: int, k: int, E: int, H: int, I: int, gate: ExpertTables, up: ExpertTables,
@@ -381,9 +402,13 @@ class MoeLayer:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
 
     def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, stream=None,
-                fuse_sort: bool = True):
+                fuse_sort: bool = True, fuse_blend: Optional[bool] = None):
         """``fuse_sort``: sort and gate+up through moe_nvfp4_sort_gate_up_silu
-        (one launch for few-token decode); False issues the two calls."""
+        (one launch for few-token decode); False issues the two calls.
+        ``fuse_blend``: down and blend through moe_nvfp4_down_blend (one
+        launch, ``y`` is not written); None picks it for one token with
+        row-major weights when the library admits the shape, else the two
+        calls."""
         s = _stream(stream)
         if self.gate_up is not None:
             moe_nvfp4_sort(topk_ids, self.E, self.expert_offsets, self.sorted_token_ids, self.pair_pos,
@@ -400,6 +425,19 @@ class MoeLayer:
                            self.active_experts, self.active_count, self.err_flag, s)
             moe_nvfp4_gate_up_silu(x, self.k, self.E, self.H, self.I, self.gate, self.up, self.expert_offsets,
                                    self.sorted_token_ids, self.active_experts, self.active_count, self.h, s)
+        if fuse_blend is None:
+            fuse_blend = self.T == 1 and self.down.layout == ROW_MAJOR
+            if fuse_blend:
+                rc = _down_blend_rc(self.h, topk_ids, topk_weights, self.pair_pos, self.E, self.H, self.I,
+                                    self.down, self.out, s)
+                if rc == 0:
+                    return self.out
+                if rc != _ELIMIT:  # ELIMIT: the shape is not admitted; issue the two calls
+                    _check("moe_nvfp4_down_blend", rc)
+        elif fuse_blend:
+            moe_nvfp4_down_blend(self.h, topk_ids, topk_weights, self.pair_pos, self.E, self.H, self.I,
+                                 self.down, self.out, s)
+            return self.out
         moe_nvfp4_down(self.h, self.T, self.k, self.E, self.H, self.I, self.down, self.expert_offsets,
                        self.active_experts, self.active_count, self.y, s)
         moe_nvfp4_blend(self.y, topk_weights, self.pair_pos, self.out, s)

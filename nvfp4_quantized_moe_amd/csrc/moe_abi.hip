@@ -11,6 +11,9 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
                           const moe_nvfp4_experts *B, float *out, int N, int K, int T, int P, int E,
                           hipStream_t stream, const MoeSortFuse *fuse);
 int moe_decode_sort_gate_up_launches(int N, int K, int P, int E);
+int moe_launch_down_blend(const float *h, const int32_t *topk_ids, const float *topk_weights,
+                          const int32_t *pair_pos, const moe_nvfp4_experts &D, uint16_t *out, int N, int K, int T,
+                          int k, int E, hipStream_t stream);
 int moe_launch_sort(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets, int32_t *sorted_tok,
                     int32_t *pair_pos, int32_t *active, int32_t *active_count, uint32_t *err_flag,
                     hipStream_t stream);
@@ -125,4 +128,16 @@ extern "C" int moe_nvfp4_down(const float *h, int32_t T, int32_t k, int32_t E, i
     return moe_launch_gemm_kmajor(false, down.layout == MOE_NVFP4_K_MAJOR_MXFP4, h, nullptr, expert_offsets,
                                   active_experts, active_count, down, nullptr, y, H, I, P, E, H, 0,
                                   (hipStream_t)stream);
+}
+
+extern "C" int moe_nvfp4_down_blend(const float *h, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                    moe_nvfp4_experts down, const int32_t *topk_ids, const float *topk_weights,
+                                    const int32_t *pair_pos, uint16_t *out, void *stream) {
+    if (!h || !topk_ids || !topk_weights || !pair_pos || !out) return MOE_NVFP4_ENULL;
+    if (moe_host::experts_null(down)) return MOE_NVFP4_ENULL;
+    const int rc = check_common(T, k, E, H, I, down.layout);
+    if (rc != MOE_NVFP4_OK) return rc;
+    if (down.layout != MOE_NVFP4_ROW_MAJOR) return MOE_NVFP4_ELAYOUT;
+    return moe_launch_down_blend(h, topk_ids, topk_weights, pair_pos, down, out, H, I, T, k, E,
+                                 (hipStream_t)stream);
 }

@@ -107,6 +107,11 @@ struct DecArgs {
     const int32_t *topk_ids;
     int32_t *sort_offsets, *sort_tok, *sort_pos, *sort_active, *sort_count;
     uint32_t *err_flag;
+    // Down projection with the blend fused in (k_decode_down_blend): the
+    // routing weights, each pair's sorted position, and the bf16 output.
+    const float *blend_w;
+    const int32_t *blend_pos;
+    uint16_t *blend_out;
 };
 
 // The fused sort's tables, in the LDS area the pass prefix would otherwise
@@ -199,13 +204,15 @@ __device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v)
 // ldx), row m scaled by 2^-e(m) where e(m) comes from the row's largest
 // magnitude (kept in rmax[m] as float bits; rmax is zero on entry).  Gate+up
 // gathers x rows by token (lane m < 16 of each wave holds row m's token in
-// tokv); down reads h rows in order.  mid() is called once the first loads
-// are in flight and before any is consumed, so the caller can queue more
-// loads behind them.  Ends with the rows visible to the whole block.
-template <bool GATED, typename Mid>
+// tokv); down reads h rows in order, or (GATHER) row gpos[m] for row m.
+// mid() is called once the first loads are in flight and before any is
+// consumed, so the caller can queue more loads behind them.  Ends with the
+// rows visible to the whole block.
+template <bool GATED, bool GATHER = false, typename Mid>
 __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int tokv, uint16_t *xs, uint32_t *rmax,
-                                      Mid &&mid) {
+                                      Mid &&mid, const int *gpos = nullptr) {
     const int K = a.K, ldx = a.ldx;
+    auto hrow = [&](int m) -> size_t { return GATHER ? (size_t)gpos[m] : (size_t)(row0 + m); };
     const int cpr = K >> 3;  // 8-element chunks per row
     const int nch = pr * cpr;
     constexpr int SB = GATED ? 8 : 4;  // chunks per thread per batch
@@ -268,7 +275,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                 int m, kc;
                 chunk(i * kThreads + (int)threadIdx.x, m, kc);
                 row[i] = m;
-                const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
+                const float *src = h + hrow(m) * K + 8 * kc;
                 f0[i] = moe::gload<f32x4_t>(src);
                 f1[i] = moe::gload<f32x4_t>(src + 4);
             }
@@ -294,7 +301,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                     int m, kc;
                     chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
                     row[i] = m;
-                    const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
+                    const float *src = h + hrow(m) * K + 8 * kc;
                     f0[i] = moe::gload<f32x4_t>(src);
                     f1[i] = moe::gload<f32x4_t>(src + 4);
                 }
@@ -316,7 +323,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
                     chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
                     dst[i] = m * ldx + 8 * kc;
                     fs[i] = exp2i(-row_exp(rmax[m]));
-                    const float *src = h + (size_t)(row0 + m) * K + 8 * kc;
+                    const float *src = h + hrow(m) * K + 8 * kc;
                     f0[i] = moe::gload<f32x4_t>(src);
                     f1[i] = moe::gload<f32x4_t>(src + 4);
                 }
@@ -1045,6 +1052,254 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     }
 }
 
+// Down projection with the top-k blend fused in, for one or a few tokens.
+//
+// The blend (out[t] = sum over j of w[t, j] * y[pair (t, j)], fp32, ascending
+// j, one rounding to bf16) needs every pair of a token at once, so here a
+// block takes one token and C = 8 G output columns of the down matrices of
+// all of that token's pairs, and the pairs' y values never leave LDS: no y
+// tensor, no blend launch, no second trip through memory.  The weights of an
+// expert are read once per token routed to it, so this suits decode with few
+// tokens (one token: every expert once).
+//   * Pairs.  Wave 0 reads the token's routed ids, sorted positions and
+//     weights, then the expert tables of the pairs that have an expert
+//     ("live": a position and non-NULL weights), and lists the live pairs in
+//     ascending j.  Live pair r belongs to wave r mod 4.
+//   * Activations.  The h rows of the live pairs (gathered by sorted
+//     position) are staged as in the grouped kernel: fp16, one power of two
+//     per row.
+//   * Stream.  Wave w streams units of 8 weight rows, (its p-th live pair,
+//     column group g), through the same register ring, lane layout and
+//     matrix-core arithmetic as the grouped kernel, so each y value is the
+//     one the grouped kernel computes for that row, bit for bit.  Unit
+//     results go to an LDS table y[live pair][column].
+//   * Blend.  After one barrier, thread n < C sums its column over the pairs
+//     in ascending j exactly as the blend kernel does (a pair whose expert is
+//     NULL adds w * 0; a pair with no expert adds nothing) and writes bf16.
+constexpr int kBlendMaxK = 64;     // pairs per token
+constexpr int kBlendMaxCols = 32;  // output columns per block (G <= 4)
+struct BlendLds {
+    const uint8_t *pa[kBlendMaxK];  // by live index: the pair's expert
+    const uint8_t *sa[kBlendMaxK];
+    float s2[kBlendMaxK];
+    int pos[kBlendMaxK];        // by live index: sorted position (h row)
+    uint32_t rmax[kBlendMaxK];  // by live index: staged row maxima
+    float w[kBlendMaxK];        // by pair j: routing weight
+    int live_of[kBlendMaxK];    // by pair j: live index; -1 NULL expert (y = 0); -2 no expert
+    int nlive;
+};
+constexpr int kBlendTblOff = kWaves * kScaleLds;
+constexpr int kBlendYOff = (kBlendTblOff + (int)sizeof(BlendLds) + 15) & ~15;
+constexpr int kBlendHdrLds = kBlendYOff + kBlendMaxK * kBlendMaxCols * 4;
+
+__global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
+    extern __shared__ uint4 lds4[];
+    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+    BlendLds *bl = reinterpret_cast<BlendLds *>(lds + kBlendTblOff);
+    float *ypart = reinterpret_cast<float *>(lds + kBlendYOff);
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds + kBlendHdrLds);
+    const int t = blockIdx.y, k = a.topk, G = a.G, C = 8 * G;
+    const int col0 = blockIdx.x * C;
+    const int lane = threadIdx.x & 63, w = moe::wave_id();
+    constexpr int D = kDepth;
+
+    if (w == 0) {  // the token's pairs: lane j holds pair j
+        int pos = -1, id = -1;
+        float wj = 0.f;
+        if (lane < k) {
+            const size_t p = (size_t)t * k + lane;
+            id = a.topk_ids[p];
+            pos = a.blend_pos[p];
+            wj = a.blend_w[p];
+        }
+        const bool routed = lane < k && pos >= 0 && id >= 0 && id < a.E;
+        const uint8_t *pa = nullptr, *sa = nullptr;
+        float s2 = 0.f;
+        if (routed) {
+            pa = a.pa[id];
+            sa = a.sa[id];
+            s2 = a.s2a[id];
+        }
+        const bool live = routed && pa != nullptr;
+        const unsigned long long lm = __ballot(live);
+        const int li = __popcll(lm & ((1ull << lane) - 1ull));
+        if (live) {
+            bl->pa[li] = pa;
+            bl->sa[li] = sa;
+            bl->s2[li] = s2;
+            bl->pos[li] = pos;
+        }
+        if (lane < k) {
+            bl->w[lane] = wj;
+            bl->live_of[lane] = live ? li : (routed ? -1 : -2);
+        }
+        bl->rmax[lane] = 0u;
+        if (lane == 0) bl->nlive = __popcll(lm);
+    }
+    __syncthreads();
+    const int nlive = bl->nlive;
+
+    if (nlive > 0) {
+        const int K = a.K, ldx = a.ldx;
+        const int rowbytes = K >> 1, sbytes = K >> 4;
+        const int nseg = (rowbytes + kSegBytes - 1) / kSegBytes;
+        const int npw = nlive > w ? (nlive - 1 - w) / kWaves + 1 : 0;  // live pairs w, w + 4, ...
+        const int nu = npw * G;                                          // units (pair p, group g)
+        const int total = nu * nseg;
+        const int n = lane & 15, q = lane >> 4;
+        const int rho = n >> 2, c = n & 3;
+        const int choff = 64 * q + 16 * c;
+        const int s4 = lane >> 4, r8 = (lane >> 1) & 7, hh = lane & 1;
+        uint8_t *sc_lds = lds + w * kScaleLds;
+
+        u32x4_t w0[D], w1[D], sv[D / kGroup];
+        int ssh[D / kGroup];
+        int lu = 0, li = 0, lp = 0, lg = 0;  // next load: unit lu = (pair lp, group lg), segment li
+        auto load = [&](int d) {
+            if (d % kGroup == 0) {
+                // Scale slice of step (lu, li) + s4 for row r8 of the unit (16 bytes, half hh).
+                int l = li + s4, u = lu, p = lp, g = lg;
+#pragma unroll
+                for (int i = 0; i < kGroup - 1; ++i) {
+                    const bool wrap = l >= nseg;
+                    l = wrap ? l - nseg : l;
+                    u = wrap ? u + 1 : u;
+                    g = wrap ? g + 1 : g;
+                    p = g == G ? p + 1 : p;
+                    g = g == G ? 0 : g;
+                }
+                const bool real = u < nu;
+                p = real ? p : npw - 1;
+                g = real ? g : G - 1;
+                l = real ? l : nseg - 1;
+                const int want = 32 * l + 16 * hh;
+                const int got = min(want, sbytes - 16);
+                ssh[d / kGroup] = (want - got) >> 2;
+                const uint8_t *sk = bl->sa[w + kWaves * p];
+                sv[d / kGroup] = moe::gload<u32x4_t>(sk + (size_t)(col0 + 8 * g + r8) * sbytes + got);
+            }
+            const bool real = lu < nu;  // past the end: the last real step again
+            const int p = real ? lp : npw - 1, g = real ? lg : G - 1;
+            const int off = min(kSegBytes * (real ? li : nseg - 1) + choff, rowbytes - 16);
+            const uint8_t *pk = bl->pa[w + kWaves * p] + (size_t)(col0 + 8 * g + rho) * rowbytes + off;
+            w0[d] = moe::gload<u32x4_t>(pk);
+            w1[d] = moe::gload<u32x4_t>(pk + (size_t)4 * rowbytes);
+            if (++li == nseg) {
+                li = 0;
+                ++lu;
+                if (++lg == G) {
+                    lg = 0;
+                    ++lp;
+                }
+            }
+        };
+
+        stage<false, true>(
+            a, 0, nlive, 0, xs, bl->rmax,
+            [&]() {
+                __builtin_amdgcn_sched_barrier(0);
+                if (nu > 0) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        load(d);
+                        __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+                    }
+                }
+            },
+            bl->pos);
+
+        if (nu > 0) {
+            const int cA = n & 3;
+            const int sread0 = 32 * rho + 8 * q + 2 * c;
+            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            int cu = 0, ci = 0, cp = 0, cg = 0;  // stream position being computed
+            auto step = [&](const int d, auto refill) {
+                if (d % kGroup == 0) {
+                    const u32x4_t v = sv[d / kGroup];
+                    const int s = ssh[d / kGroup];
+                    u32x4_t r;
+                    r[0] = s == 0 ? v[0] : (s == 1 ? v[1] : (s == 2 ? v[2] : v[3]));
+                    r[1] = s == 0 ? v[1] : (s == 1 ? v[2] : v[3]);
+                    r[2] = s == 0 ? v[2] : v[3];
+                    r[3] = v[3];
+                    *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
+                }
+                const int rl = w + kWaves * (cu < nu ? cp : npw - 1);  // live row of this unit
+                const int ka = 512 * ci + 128 * q + 32 * cA;
+                const int kac = ka < K ? ka : 0;
+                f16x8_t a0[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + rl * ldx + kac + 8 * ks);
+                const int kq = 512 * ci + 128 * q + 32 * c;
+                const bool kin = cu < nu && kq < K;
+                const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
+                const uint32_t v0 = *reinterpret_cast<const uint16_t *>(sp);
+                const uint32_t v1 = *reinterpret_cast<const uint16_t *>(sp + 128);
+                const f16x2_t zero2 = {(_Float16)0.f, (_Float16)0.f};
+                const f16x2_t sf0 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v0, 1.0f, false) : zero2;
+                const f16x2_t sf1 = kin ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v1, 1.0f, false) : zero2;
+                const f16x2_t sl0 = {sf0.x, sf0.x}, sh0 = {sf0.y, sf0.y};
+                const f16x2_t sl1 = {sf1.x, sf1.x}, sh1 = {sf1.y, sf1.y};
+                f16x8_t b0[4], b1[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    b0[ks] = decode_b(w0[d][ks], ks < 2 ? sl0 : sh0);
+                    b1[ks] = decode_b(w1[d][ks], ks < 2 ? sl1 : sh1);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b0[ks], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1, 0, 0, 0);
+                }
+                if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
+                    // Token rows 0 of the quad sums (every A row holds the pair's h row).
+                    const float oscale = exp2i(row_exp(bl->rmax[rl]));
+                    const float s2 = bl->s2[rl];
+                    const float g0 = moe::group_sum<4>(pick(acc0, c)) * oscale;
+                    const float g1 = moe::group_sum<4>(pick(acc1, c)) * oscale;
+                    if (c == 0 && q == 0) {
+                        ypart[rl * C + 8 * cg + rho] = g0 * s2;
+                        ypart[rl * C + 8 * cg + 4 + rho] = g1 * s2;
+                    }
+                    acc0 = acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                if (++ci == nseg) {
+                    ci = 0;
+                    ++cu;
+                    if (++cg == G) {
+                        cg = 0;
+                        ++cp;
+                    }
+                }
+                if constexpr (decltype(refill)::value) {
+                    __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
+                    load(d);
+                    __builtin_amdgcn_sched_barrier(kMoveAcrossLoads);
+                }
+            };
+            int base = 0;
+            for (; base + D < total; base += D) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) step(d, std::true_type{});
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d) step(d, std::false_type{});
+        }
+    }
+    __syncthreads();  // every live pair's y columns are in LDS
+    if ((int)threadIdx.x < C) {
+        const int col = threadIdx.x;
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int r = bl->live_of[j];
+            if (r == -2) continue;
+            acc = fmaf(bl->w[j], r >= 0 ? ypart[r * C + col] : 0.f, acc);
+        }
+        a.blend_out[(size_t)t * a.N + col0 + col] = moe::f32_to_bf16_rne(acc);
+    }
+}
+
 }  // namespace
 
 // Launch the row-major grouped projection (used by the two C-ABI entry points).
@@ -1070,11 +1325,14 @@ DecConfig decode_config(bool gated, int N, int K, int P, int E) {
     c.units = (N + ucols - 1) / ucols;
     const int cap = E < P ? E : P;
     // Units per block: about 32 ring steps per wave, so a block's start-up
-    // (tables, activation staging, first loads) is paid over enough streaming;
-    // fewer when the grid would otherwise not fill two blocks per CU.
+    // (tables, activation staging, first loads) is paid over enough streaming,
+    // but at most 6: on short rows (K about 2048) 8 units per block measured
+    // 3-8% slower on the down projection than 6 (fewer, longer blocks leave a
+    // longer tail), and 4 or fewer paid the start-up too often.  Fewer still
+    // when the grid would otherwise not fill two blocks per CU.
     const int nseg = (K / 2 + 255) / 256;
     int G = (32 + nseg - 1) / nseg;
-    G = G < 1 ? 1 : (G > 8 ? 8 : G);
+    G = G < 1 ? 1 : (G > 6 ? 6 : G);
     while (G > 1 && (int64_t)cap * ((c.units + G - 1) / G) < 2 * (int64_t)moe_host::cu_count()) --G;
     c.G = G;
     // Staged row stride: 2K bytes padded to 16 mod 256, so the 16 lanes of an
@@ -1187,5 +1445,40 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
         hipLaunchKernelGGL((k_decode_row<true, false>), grid, dim3(kThreads), lds, stream, a);
     else
         hipLaunchKernelGGL((k_decode_row<false, false>), grid, dim3(kThreads), lds, stream, a);
+    return moe_host::launch_status();
+}
+
+// Down projection with the blend fused in (moe_nvfp4_down_blend): one block
+// per (C output columns, token).  ELIMIT when k > 64, T > 65535, or the
+// token's k activation rows do not fit the staging budget.
+int moe_launch_down_blend(const float *h, const int32_t *topk_ids, const float *topk_weights,
+                          const int32_t *pair_pos, const moe_nvfp4_experts &D, uint16_t *out, int N, int K, int T,
+                          int k, int E, hipStream_t stream) {
+    if (k > kBlendMaxK || T > 65535) return MOE_NVFP4_ELIMIT;
+    DecArgs a = {};
+    a.act = h;
+    a.pa = D.packed;
+    a.sa = D.scale;
+    a.s2a = D.scale2;
+    a.N = N;
+    a.K = K;
+    a.topk = k;
+    a.E = E;
+    a.topk_ids = topk_ids;
+    a.blend_w = topk_weights;
+    a.blend_pos = pair_pos;
+    a.blend_out = out;
+    const int pad_bytes = ((16 - (2 * K) % 256) + 256) % 256;
+    a.ldx = K + pad_bytes / 2;
+    const size_t rows_lds = (size_t)k * (size_t)a.ldx * 2;
+    if (rows_lds > (size_t)kLdsBudget) return MOE_NVFP4_ELIMIT;
+    // Columns per block: 8 G, G doubled (up to 4) while the grid still holds
+    // two blocks per CU, so the h rows staged per block serve more weights.
+    int G = 1;
+    while (G < 4 && (int64_t)(N / (16 * G)) * T >= 2 * (int64_t)moe_host::cu_count()) G *= 2;
+    a.G = G;
+    const size_t lds = (size_t)kBlendHdrLds + rows_lds;
+    hipLaunchKernelGGL(k_decode_down_blend, dim3((unsigned)(N / (8 * G)), (unsigned)T), dim3(kThreads), lds, stream,
+                       a);
     return moe_host::launch_status();
 }

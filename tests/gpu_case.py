@@ -114,9 +114,11 @@ class Case:
 
         return fn
 
-    def run(self):
+    def run(self, fuse_blend: bool = False):
+        """One forward; by default down and blend as two calls, so y is there
+        to check."""
         self.layer.err_flag.zero_()
-        out = self.layer.forward(self.x, self.ids_d, self.w_d)
+        out = self.layer.forward(self.x, self.ids_d, self.w_d, fuse_blend=fuse_blend)
         torch.cuda.synchronize()
         return out
 

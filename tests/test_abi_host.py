@@ -18,10 +18,10 @@ def test_library_exports_every_header_function():
     assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                           "transpose_u8", "moe_nvfp4_abi_version", "moe_nvfp4_route", "transpose_u8_pitched",
                           "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
-                          "moe_nvfp4_sort_gate_up_launches"}
+                          "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 5
+    assert L.moe_nvfp4_abi_version() == 6
 
 
 def _ex(layout=0, null=False):
@@ -148,6 +148,25 @@ def test_sort_gate_up_launch_count_query():
     assert L.moe_nvfp4_sort_gate_up_launches(2048, 4, 64, 4096, 1536, 1) == 2
     assert L.moe_nvfp4_sort_gate_up_launches(4, 2, 4, 256, 512, 7) == ELAYOUT
     assert L.moe_nvfp4_sort_gate_up_launches(4, 5, 4, 256, 512, 0) == ESHAPE
+
+
+def test_down_blend_rejects():
+    L = moe.lib()
+
+    def call(h=D, T=1, k=8, E=128, H=2048, I=768, d=None, ids=D, w=D, pos=D, out=D):
+        return L.moe_nvfp4_down_blend(h, T, k, E, H, I, d or _ex(), ids, w, pos, out, None)
+
+    for kw in ("h", "ids", "w", "pos", "out"):
+        assert call(**{kw: None}) == ENULL
+    assert call(d=_ex(null=True)) == ENULL
+    assert call(d=_ex(1)) == ELAYOUT                    # row-major weights only
+    assert call(d=_ex(2)) == ELAYOUT
+    assert call(I=500) == ESHAPE
+    assert call(k=129) == ESHAPE                        # k > E
+    assert call(k=65, E=256) == ELIMIT                  # more pairs than a block takes
+    assert call(T=65536) == ELIMIT                      # one block row per token
+    assert call(k=64, E=64, H=256, I=2048) == ELIMIT    # 64 staged rows of 2 I bytes exceed the budget
+    assert call(k=36, E=64, H=256, I=1024) == ELIMIT    # 36 rows of 2064 bytes > 73728 (35 would fit)
 
 
 def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):

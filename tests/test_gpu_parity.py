@@ -531,6 +531,74 @@ def test_sort_fused_into_gate_up_matches_two_calls(T, k, E, H, I, mode):
     assert torch.equal(h_f[:n], h_u[:n])
 
 
+# ---------------------------------------------------------------- down + blend in one launch
+@pytest.mark.parametrize("T,H,I,E,k,mode", [
+    (1, 2048, 768, 128, 8, "cfg"),      # the 1-token decode workload itself
+    (1, 256, 512, 4, 2, "rand"),
+    (1, 512, 256, 16, 1, "rand"),       # one pair: three waves stream nothing
+    (1, 320, 448, 9, 5, "dup"),         # one expert twice, ragged widths
+    (1, 256, 256, 80, 64, "rand"),      # k = 64, the most pairs a block takes
+    (1, 640, 384, 12, 6, "null"),       # a NULL expert among the pairs
+    (2, 256, 512, 8, 3, "invalid"),     # ids outside [0, E) add nothing
+    (5, 2048, 256, 64, 4, "rand"),      # two column groups per block
+    (32, 2688, 1856, 128, 6, "zipf"),   # many tokens: four column groups, experts shared
+])
+def test_down_blend_matches_down_then_blend(T, H, I, E, k, mode):
+    """moe_nvfp4_down_blend against moe_nvfp4_down + moe_nvfp4_blend on the
+    same h: bit for bit while every expert holds at most 4 routed pairs (the
+    grouped kernel then computes each y value in the same order), and against
+    the oracle's layer output in every case."""
+    say("down+blend", T, H, I, E, k, mode)
+    if mode == "cfg":
+        case = Case(2)
+    else:
+        routing = "zipf" if mode == "zipf" else "uniform"
+        shape = synth.MoeShape(f"db_{T}_{k}_{E}", T, H, I, E, k, routing, False)
+        ids, w = synth.gen_routing(25, shape)
+        nulls = ()
+        if mode == "dup":
+            ids[0, 1] = ids[0, 0]
+        elif mode == "invalid":
+            ids[0, 0] = -1
+            ids[1, 2] = E + 3
+        elif mode == "null":
+            nulls = (int(ids[0, 1]),)
+        case = Case(25, shape, ids=ids, weights=w, nulls=nulls)
+    s, L = case.shape, case.layer
+    case.run(fuse_blend=False)
+    fused = torch.full_like(L.out, 7.0)
+    moe.moe_nvfp4_down_blend(L.h, case.ids_d, case.w_d, L.pair_pos, s.E, s.H, s.I, L.down, fused)
+    torch.cuda.synchronize()
+    rows = np.diff(L.expert_offsets.cpu().numpy())
+    if rows.max() <= 4:
+        assert torch.equal(fused.view(torch.int16), L.out.view(torch.int16))
+    ref = oracle.moe_layer(case.x_bits, case.ids, case.w, case.weight_fn(), s.E, s.H, s.I)
+    e = parity.assert_parity(_h2f(fused), ref["out"], f"down+blend {T},{H},{I},{E},{k},{mode}")
+    say("down+blend", mode, "max rows per expert", int(rows.max()), e)
+
+
+def test_layer_one_token_fuses_down_blend_or_falls_back():
+    """MoeLayer.forward with one token: down and blend in one launch (y left
+    untouched); a shape whose 64 activation rows do not fit the staging
+    budget (k = 64, I = 2048) is refused with ELIMIT and the layer issues the
+    two calls instead (y written).  Both match the oracle."""
+    say("layer one token: fused down+blend / fallback")
+    for (H, I, E, k), fused in (((2048, 768, 128, 8), True), ((256, 2048, 64, 64), False)):
+        shape = synth.MoeShape(f"one_tok_{k}", 1, H, I, E, k, "uniform", False)
+        case = Case(26, shape)
+        L = case.layer
+        L.y.fill_(3.0)
+        out = L.forward(case.x, case.ids_d, case.w_d)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(case.x_bits, case.ids, case.w, case.weight_fn(), E, H, I)
+        parity.assert_parity(_h2f(out), ref["out"], f"one token k={k}")
+        y_touched = bool((L.y != 3.0).any().item())
+        assert y_touched != fused, (k, fused)
+        if not fused:
+            with pytest.raises(moe.MoeNvfp4Error, match="ELIMIT"):
+                moe.moe_nvfp4_down_blend(L.h, case.ids_d, case.w_d, L.pair_pos, E, H, I, L.down, L.out)
+
+
 # ---------------------------------------------------------------- graph capture
 def test_layer_graph_replays_match_eager():
     """The decode layer (sort fused into gate+up) captured in a HIP graph: every
