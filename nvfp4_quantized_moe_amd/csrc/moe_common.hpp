@@ -68,6 +68,18 @@ __device__ __forceinline__ T gload(const void *p) {
     }
 }
 
+// 16-byte load with the nontemporal hint, for weight bytes that are streamed
+// once: they then do not displace reused data (activations, weights that a
+// later pass reads again) from the caches.
+template <typename T>
+__device__ __forceinline__ T gload_nt(const void *p) {
+    static_assert(sizeof(T) == 16, "16-byte loads only");
+    const u32x4_t v = __builtin_nontemporal_load((const MOE_GLOBAL u32x4_t *)p);
+    T t;
+    __builtin_memcpy(&t, &v, 16);
+    return t;
+}
+
 // Index of this wavefront in the block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

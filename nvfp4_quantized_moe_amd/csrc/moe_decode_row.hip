@@ -100,6 +100,7 @@ struct DecArgs {
     int ldx;                    // staged row stride, fp16 elements
     int extra;                  // block rows for passes beyond each expert's first
     int single_token;           // gate+up with T == 1: every routed row is token 0
+    int nt_min_active;          // nontemporal weight loads from this many active experts on
     // Routing sort fused into the gate+up launch (few pairs, one pass per
     // expert): the routed ids, and the sort outputs that block (0, 0) writes.
     int fused_sort;
@@ -147,6 +148,22 @@ __device__ __forceinline__ float pick(const f32x4_t &v, int i) {
     r = i == 2 ? v[2] : r;
     r = i == 3 ? v[3] : r;
     return r;
+}
+
+// A 16-byte weight load; NT: the nontemporal hint.  It is used when the
+// launch streams more expert weights than the 256 MB Infinity Cache holds
+// (caching them cannot pay off), only for experts read by one pass (a later
+// pass finds the weights of a busy expert in the cache), and only in the
+// (row, quarter) pass: 64 tokens x 256 experts (3.7 GB of gate+up weights)
+// ran 8% faster in gate+up and 5% in down so, while the hint in the
+// token-dense pass as well gave back most of the gate+up gain, and 32 tokens
+// (170 MB) ran 4-6% slower with it, hence the size bound.
+template <bool NT>
+__device__ __forceinline__ u32x4_t wload(const void *p) {
+    if constexpr (NT)
+        return moe::gload_nt<u32x4_t>(p);
+    else
+        return moe::gload<u32x4_t>(p);
 }
 
 // Power-of-two exponent e that brings a row maximum (bits of a non-negative
@@ -338,7 +355,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
 // One pass: rows [row0, row0 + pr) of the expert against units
 // [u_first, u_first + nu) of its weights.
 // A pass of up to 4 rows in the (row, quarter) layout.
-template <bool GATED, int D, bool TOK_LDS>  // TOK_LDS: pass tokens from the fused sort's LDS table
+template <bool GATED, int D, bool TOK_LDS, bool NT>  // TOK_LDS: pass tokens from the fused sort's LDS table
 __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                          const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
                                          const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
@@ -399,8 +416,8 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
         const bool real = lu < nu;  // past the end: the last real step again
         const int unit = u_first + (real ? lu : nu - 1);
         const int off = min(kSegBytes * (real ? li : nseg - 1) + choff, rowbytes - 16);
-        w0[d] = moe::gload<u32x4_t>(wb0 + (size_t)unit * ustride + off);
-        w1[d] = moe::gload<u32x4_t>(wb1 + (size_t)unit * ustride + off);
+        w0[d] = wload<NT>(wb0 + (size_t)unit * ustride + off);
+        w1[d] = wload<NT>(wb1 + (size_t)unit * ustride + off);
         if (++li == nseg) {
             li = 0;
             ++lu;
@@ -784,9 +801,9 @@ __device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
 }
 
 // One pass of expert e, whose rows are the sorted positions [lo, hi).
-template <bool GATED, bool TOK_LDS>
+template <bool GATED, bool TOK_LDS, bool NT_OK>  // NT_OK: built with the nontemporal variant
 __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, int hi, int pass, int u_first,
-                                             int nu, uint8_t *lds) {
+                                             int nu, bool nt_ok, uint8_t *lds) {
     // Every table entry of expert e is read at once (e < E, so each read is
     // in bounds): one round of dependent loads, not one per table.
     const uint8_t *pA = a.pa[e];
@@ -812,17 +829,23 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
     }
     // Passes of more than 4 rows (more than one token group) run token-dense:
     // one MFMA per 16 rows instead of one per 4.
+    // Nontemporal weight loads: a large launch, and an expert read by this
+    // pass alone.
     if (pr > 4)
         run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+    else if (NT_OK && nt_ok && rows <= a.pass_rows)
+        run_pass<GATED, kDepth, TOK_LDS, NT_OK>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
     else
-        run_pass<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+        run_pass<GATED, kDepth, TOK_LDS, false>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
 }
 
-template <bool GATED>
-__device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, uint8_t *lds) {
+template <bool GATED, bool NT_OK>
+__device__ __forceinline__ void do_pass(const DecArgs &a, int slot, int pass, int u_first, int nu, int nactive,
+                                        uint8_t *lds) {
     const int e = a.active[slot];  // -1 past the active count
     if (e < 0) return;
-    do_pass_rows<GATED, false>(a, e, a.offsets[e], a.offsets[e + 1], pass, u_first, nu, lds);
+    const bool nt_ok = a.nt_min_active > 0 && nactive >= a.nt_min_active;
+    do_pass_rows<GATED, false, NT_OK>(a, e, a.offsets[e], a.offsets[e + 1], pass, u_first, nu, nt_ok, lds);
 }
 
 // Routing sort of P <= 64 pairs inside the block (the sort step fused into
@@ -905,11 +928,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     if constexpr (GATED && SORT) {  // extra == 0: one pass per expert
         const int3 r = fused_sort(a, reinterpret_cast<SortLds *>(lds + kPreOff), y);
         if (r.x < 0) return;  // past the active count
-        do_pass_rows<GATED, true>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, lds);
+        do_pass_rows<GATED, true, false>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, false, lds);
         return;
     }
     if (y >= a.extra) {
-        do_pass<GATED>(a, y - a.extra, 0, u_first, nu, lds);
+        // The nontemporal variant serves the down projection here; large
+        // gate+up launches run persistent.
+        do_pass<GATED, !GATED>(a, y - a.extra, 0, u_first, nu, GATED ? 0 : *a.nactive, lds);
         return;
     }
     int *pre = reinterpret_cast<int *>(lds + kPreOff);
@@ -919,7 +944,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     for (int g = y; g < total; g += a.extra) {
         const int slot = find_slot(pre, n, g);
         if (g > y) __syncthreads();  // the previous pass's readers of LDS are done
-        do_pass<GATED>(a, slot, 1 + g - pre[slot], u_first, nu, lds);
+        do_pass<GATED, !GATED>(a, slot, 1 + g - pre[slot], u_first, nu, n, lds);
     }
 }
 
@@ -1041,7 +1066,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         const int ub = last_item ? end.u : a.units;
         if (!first) __syncthreads();  // the previous pass's readers of LDS are done
         first = false;
-        do_pass<GATED>(a, k.s, k.p, k.u, ub - k.u, lds);
+        do_pass<GATED, true>(a, k.s, k.p, k.u, ub - k.u, n, lds);
         // next (slot, pass)
         const int r = slot_rows(a, k.s);
         if ((k.p + 1) * a.pass_rows < r) {
@@ -1396,6 +1421,10 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.N = N;
     a.K = K;
     a.single_token = gated && T == 1;
+    // Nontemporal weight loads once the active experts' weights of this
+    // projection exceed the 256 MB Infinity Cache.
+    const int64_t expert_bytes = (gated ? 2 : 1) * (int64_t)N * (K / 2 + K / 16);
+    a.nt_min_active = (int)(((int64_t)256 << 20) / expert_bytes + 1);
     const DecConfig c = decode_config(gated, N, K, P, E);
     if (!c.ok) return MOE_NVFP4_ELIMIT;
     a.units = c.units;
