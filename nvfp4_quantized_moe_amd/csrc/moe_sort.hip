@@ -152,25 +152,35 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
     for (int p = total + tid; p < P; p += kSortThreads) sorted_tok[p] = -1;
 }
 
-// Few pairs (P <= 64): one pair per lane of wave 0, one LDS histogram, no
-// second read of the ids.  Same results as k_moe_sort.
+// Few pairs (P <= 256): one pair per thread, an LDS histogram of all pairs
+// and one per wave, no second read of the ids.  A pair's position is its
+// expert's offset, plus the pairs of its id in earlier waves, plus those in
+// earlier lanes of its own wave.  Same results as k_moe_sort.
 constexpr int kSmallThreads = 256;
-constexpr int kSmallPairs = 64;
+constexpr int kSmallPairs = kSmallThreads;
+constexpr int kSmallWaves = kSmallThreads / 64;
 
 __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     const int32_t *__restrict__ ids, int P, int k, int E, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_tok, int32_t *__restrict__ pair_pos, int32_t *__restrict__ active,
     int32_t *__restrict__ active_count, uint32_t *__restrict__ err_flag) {
     __shared__ int cnt[MOE_NVFP4_MAX_EXPERTS];
-    __shared__ int wsum[2][kSmallThreads / 64];
+    __shared__ int cntw[kSmallWaves][MOE_NVFP4_MAX_EXPERTS];  // per-wave histograms
+    __shared__ int wsum[2][kSmallWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = tid < P ? ids[tid] : -1;
     const bool valid = tid < P && e >= 0 && e < E;
-    for (int i = tid; i < E; i += kSmallThreads) cnt[i] = 0;
-    if (wave == 0 && __ballot(tid < P && !valid) != 0ull && lane == 0)
-        atomicOr(err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
+    for (int i = tid; i < E; i += kSmallThreads) {
+        cnt[i] = 0;
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) cntw[w][i] = 0;
+    }
+    if (__ballot(tid < P && !valid) != 0ull && lane == 0) atomicOr(err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
     __syncthreads();
-    if (valid) atomicAdd(&cnt[e], 1);
+    if (valid) {
+        atomicAdd(&cnt[e], 1);
+        atomicAdd(&cntw[wave][e], 1);
+    }
     __syncthreads();
 
     // Exclusive scans over the experts (4 consecutive per thread) of the
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     __syncthreads();
     int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
 #pragma unroll
-    for (int w = 0; w < kSmallThreads / 64; ++w) {
+    for (int w = 0; w < kSmallWaves; ++w) {
         if (w < wave) {
             b0 += wsum[0][w];
             b1 += wsum[1][w];
@@ -225,10 +235,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     }
     __syncthreads();
 
-    if (wave == 0) {
-        // Stable rank among equal ids: lanes are in flat pair order.
+    if (wave * 64 < P) {
+        // Stable rank among equal ids: threads are in flat pair order.
         const unsigned long long lt = (1ull << lane) - 1ull;
-        const int rank = __popcll(moe::match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
+        int rank = __popcll(moe::match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
+        if (valid)
+            for (int w = 0; w < wave; ++w) rank += cntw[w][e];
         if (tid < P) {
             const int pos = valid ? cnt[e] + rank : -1;
             pair_pos[tid] = pos;

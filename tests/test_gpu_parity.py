@@ -88,10 +88,14 @@ def test_sort_configs_bit_exact(cfg):
 @pytest.mark.parametrize("T,k,E,mode", [(1, 1, 1, "rand"), (3, 4, 5, "dup"), (9, 3, 7, "invalid"),
                                          (16384, 8, 256, "rand"), (2048, 4, 1024, "rand"), (512, 1, 1024, "skew"),
                                          (100, 8, 8, "all_same"), (1000, 3, 50, "rand"),
-                                         (5000, 7, 300, "invalid"), (1 << 19, 8, 1024, "rand")])
+                                         (5000, 7, 300, "invalid"), (1 << 19, 8, 1024, "rand"),
+                                         (65, 1, 7, "rand"), (16, 8, 40, "dup"), (32, 6, 128, "invalid"),
+                                         (85, 3, 3, "invalid"), (51, 5, 1024, "rand"), (64, 4, 9, "all_same"),
+                                         (257, 1, 33, "rand")])
 def test_sort_edge_cases_bit_exact(T, k, E, mode):
     """Includes the maximum sizes: 2^22 pairs (MOE_NVFP4_MAX_PAIRS) over 1024
-    experts (MOE_NVFP4_MAX_EXPERTS)."""
+    experts (MOE_NVFP4_MAX_EXPERTS), and pair counts on both sides of the
+    single-block kernel's 64-pairs-per-wave boundaries (65 .. 257)."""
     say("sort edge", T, k, E, mode)
     rng = np.random.default_rng(T * 31 + k * 7 + E)
     ids = rng.integers(0, E, (T, k)).astype(np.int32)
