@@ -131,16 +131,34 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, numel: int = 0) -> int:
+    """Device pointer of t after checking its type, size (at least ``numel``
+    elements: the kernels read or write that many), placement and layout."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
     if not t.is_cuda:
         raise ValueError(f"{name}: expected a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous tensor")
     return t.data_ptr()
+
+
+def _x_ptr(x: torch.Tensor, numel: int) -> int:
+    """x as bf16, or as int16 holding bf16 bits."""
+    if x.dtype == torch.int16:
+        return _dev(x, torch.int16, "x (bf16 bits)", numel)
+    return _dev(x, torch.bfloat16, "x", numel)
+
+
+def _out_ptr(out: torch.Tensor, numel: int) -> int:
+    """The bf16 output, or int16 holding bf16 bits."""
+    if out.dtype == torch.int16:
+        return _dev(out, torch.int16, "out (bf16 bits)", numel)
+    return _dev(out, torch.bfloat16, "out", numel)
 
 
 class ExpertTables:
@@ -179,28 +197,29 @@ class ExpertTables:
 def moe_nvfp4_sort(topk_ids, E, expert_offsets, sorted_token_ids, pair_pos, active_experts,
                    active_count, err_flag, stream=None) -> None:
     T, k = topk_ids.shape
+    P = T * k
     rc = lib().moe_nvfp4_sort(
         _dev(topk_ids, torch.int32, "topk_ids"), T, k, E,
-        _dev(expert_offsets, torch.int32, "expert_offsets"),
-        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
-        _dev(pair_pos, torch.int32, "pair_pos"),
-        _dev(active_experts, torch.int32, "active_experts"),
-        _dev(active_count, torch.int32, "active_count"),
-        _dev(err_flag, torch.int32, "err_flag"), _stream(stream))
+        _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids", P),
+        _dev(pair_pos, torch.int32, "pair_pos", P),
+        _dev(active_experts, torch.int32, "active_experts", E),
+        _dev(active_count, torch.int32, "active_count", 1),
+        _dev(err_flag, torch.int32, "err_flag", 1), _stream(stream))
     _check("moe_nvfp4_sort", rc)
 
 
 def moe_nvfp4_gate_up_silu(x, k, E, H, I, gate: ExpertTables, up: ExpertTables, expert_offsets,
                            sorted_token_ids, active_experts, active_count, h, stream=None) -> None:
     T = x.shape[0]
+    P = T * k
     rc = lib().moe_nvfp4_gate_up_silu(
-        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
-        T, k, E, H, I, gate.abi(), up.abi(),
-        _dev(expert_offsets, torch.int32, "expert_offsets"),
-        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
-        _dev(active_experts, torch.int32, "active_experts"),
-        _dev(active_count, torch.int32, "active_count"),
-        _dev(h, torch.float32, "h"), _stream(stream))
+        _x_ptr(x, T * H), T, k, E, H, I, gate.abi(), up.abi(),
+        _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids", P),
+        _dev(active_experts, torch.int32, "active_experts", E),
+        _dev(active_count, torch.int32, "active_count", 1),
+        _dev(h, torch.float32, "h", P * I), _stream(stream))
     _check("moe_nvfp4_gate_up_silu", rc)
 
 
@@ -209,17 +228,17 @@ def moe_nvfp4_sort_gate_up_silu(topk_ids, x, E, H, I, gate: ExpertTables, up: Ex
                                 stream=None) -> None:
     """Sort then gate+up (one launch in the few-token decode case); see the C header."""
     T, k = topk_ids.shape
+    P = T * k
     rc = lib().moe_nvfp4_sort_gate_up_silu(
-        _dev(topk_ids, torch.int32, "topk_ids"),
-        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
+        _dev(topk_ids, torch.int32, "topk_ids"), _x_ptr(x, T * H),
         T, k, E, H, I, gate.abi(), up.abi(),
-        _dev(expert_offsets, torch.int32, "expert_offsets"),
-        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
-        _dev(pair_pos, torch.int32, "pair_pos"),
-        _dev(active_experts, torch.int32, "active_experts"),
-        _dev(active_count, torch.int32, "active_count"),
-        _dev(err_flag, torch.int32, "err_flag"),
-        _dev(h, torch.float32, "h"), _stream(stream))
+        _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids", P),
+        _dev(pair_pos, torch.int32, "pair_pos", P),
+        _dev(active_experts, torch.int32, "active_experts", E),
+        _dev(active_count, torch.int32, "active_count", 1),
+        _dev(err_flag, torch.int32, "err_flag", 1),
+        _dev(h, torch.float32, "h", P * I), _stream(stream))
     _check("moe_nvfp4_sort_gate_up_silu", rc)
 
 
@@ -236,25 +255,26 @@ def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, e
     """Gate+up over a concatenated gate||up K-major twin (rows ``pitch``
     bytes apart, up columns from I on); see the C header."""
     T = x.shape[0]
+    P = T * k
     rc = lib().moe_nvfp4_gate_up_silu_concat(
-        _dev(x, torch.int16, "x (bf16 bits)") if x.dtype == torch.int16 else _dev(x, torch.bfloat16, "x"),
-        T, k, E, H, I, gate_up.abi(), int(pitch),
-        _dev(expert_offsets, torch.int32, "expert_offsets"),
-        _dev(sorted_token_ids, torch.int32, "sorted_token_ids"),
-        _dev(active_experts, torch.int32, "active_experts"),
-        _dev(active_count, torch.int32, "active_count"),
-        _dev(h, torch.float32, "h"), _stream(stream))
+        _x_ptr(x, T * H), T, k, E, H, I, gate_up.abi(), int(pitch),
+        _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+        _dev(sorted_token_ids, torch.int32, "sorted_token_ids", P),
+        _dev(active_experts, torch.int32, "active_experts", E),
+        _dev(active_count, torch.int32, "active_count", 1),
+        _dev(h, torch.float32, "h", P * I), _stream(stream))
     _check("moe_nvfp4_gate_up_silu_concat", rc)
 
 
 def moe_nvfp4_down(h, T, k, E, H, I, down: ExpertTables, expert_offsets, active_experts, active_count,
                    y, stream=None) -> None:
+    P = T * k
     rc = lib().moe_nvfp4_down(
-        _dev(h, torch.float32, "h"), T, k, E, H, I, down.abi(),
-        _dev(expert_offsets, torch.int32, "expert_offsets"),
-        _dev(active_experts, torch.int32, "active_experts"),
-        _dev(active_count, torch.int32, "active_count"),
-        _dev(y, torch.float32, "y"), _stream(stream))
+        _dev(h, torch.float32, "h", P * I), T, k, E, H, I, down.abi(),
+        _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
+        _dev(active_experts, torch.int32, "active_experts", E),
+        _dev(active_count, torch.int32, "active_count", 1),
+        _dev(y, torch.float32, "y", P * H), _stream(stream))
     _check("moe_nvfp4_down", rc)
 
 
@@ -262,21 +282,18 @@ def moe_nvfp4_blend(y, topk_weights, pair_pos, out, stream=None) -> None:
     T, k = topk_weights.shape
     H = y.shape[1]
     rc = lib().moe_nvfp4_blend(
-        _dev(y, torch.float32, "y"), _dev(topk_weights, torch.float32, "topk_weights"),
-        _dev(pair_pos, torch.int32, "pair_pos"), T, k, H,
-        _dev(out, torch.bfloat16, "out") if out.dtype == torch.bfloat16 else _dev(out, torch.int16, "out"),
-        _stream(stream))
+        _dev(y, torch.float32, "y", T * k * H), _dev(topk_weights, torch.float32, "topk_weights"),
+        _dev(pair_pos, torch.int32, "pair_pos", T * k), T, k, H, _out_ptr(out, T * H), _stream(stream))
     _check("moe_nvfp4_blend", rc)
 
 
 def _down_blend_rc(h, topk_ids, topk_weights, pair_pos, E, H, I, down: ExpertTables, out, stream) -> int:
     T, k = topk_weights.shape
+    P = T * k
     return lib().moe_nvfp4_down_blend(
-        _dev(h, torch.float32, "h"), T, k, E, H, I, down.abi(),
-        _dev(topk_ids, torch.int32, "topk_ids"), _dev(topk_weights, torch.float32, "topk_weights"),
-        _dev(pair_pos, torch.int32, "pair_pos"),
-        _dev(out, torch.bfloat16, "out") if out.dtype == torch.bfloat16 else _dev(out, torch.int16, "out"),
-        _stream(stream))
+        _dev(h, torch.float32, "h", P * I), T, k, E, H, I, down.abi(),
+        _dev(topk_ids, torch.int32, "topk_ids", P), _dev(topk_weights, torch.float32, "topk_weights"),
+        _dev(pair_pos, torch.int32, "pair_pos", P), _out_ptr(out, T * H), _stream(stream))
 
 
 def moe_nvfp4_down_blend(h, topk_ids, topk_weights, pair_pos, E, H, I, down: ExpertTables, out,
@@ -311,8 +328,8 @@ def moe_nvfp4_route(logits, k, topk_ids, topk_weights, stream=None) -> None:
     weights of each row of f32 logits [T, E] (see the C header)."""
     T, E = logits.shape
     rc = lib().moe_nvfp4_route(_dev(logits, torch.float32, "logits"), T, E, k,
-                               _dev(topk_ids, torch.int32, "topk_ids"),
-                               _dev(topk_weights, torch.float32, "topk_weights"), _stream(stream))
+                               _dev(topk_ids, torch.int32, "topk_ids", T * k),
+                               _dev(topk_weights, torch.float32, "topk_weights", T * k), _stream(stream))
     _check("moe_nvfp4_route", rc)
 
 

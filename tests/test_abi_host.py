@@ -93,6 +93,32 @@ def test_python_binding_checks_tensor_arguments():
         moe.transpose_u8(torch.zeros(6, dtype=torch.uint8), torch.zeros(6, dtype=torch.uint8), 2, 3)
 
 
+def test_python_binding_checks_buffer_sizes():
+    """Buffers smaller than the sizes say are refused before any launch (the
+    first argument of each call here, so the check runs before the tensors'
+    placement is looked at)."""
+    import torch
+
+    i32 = dict(dtype=torch.int32)
+    with pytest.raises(ValueError, match="y: needs at least 2048"):
+        moe.moe_nvfp4_blend(torch.zeros((7, 256)), torch.zeros((4, 2)), torch.zeros(8, **i32),
+                            torch.zeros((4, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="h: needs at least 4096"):
+        moe.moe_nvfp4_down(torch.zeros((8, 500)), 4, 2, 4, 256, 512, _Table(), torch.zeros(5, **i32),
+                           torch.zeros(4, **i32), torch.zeros(1, **i32), torch.zeros((8, 256)))
+    with pytest.raises(ValueError, match="x: needs at least 1024"):
+        moe.moe_nvfp4_gate_up_silu(torch.zeros((4, 128), dtype=torch.bfloat16), 2, 4, 256, 512, _Table(),
+                                   _Table(), torch.zeros(5, **i32), torch.zeros(8, **i32), torch.zeros(4, **i32),
+                                   torch.zeros(1, **i32), torch.zeros((8, 512)))
+
+
+class _Table:
+    """Stands in for an ExpertTables where only the argument checks run."""
+
+    def abi(self):
+        return _ex()
+
+
 def test_route_rejects():
     L = moe.lib()
     assert L.moe_nvfp4_route(None, 4, 8, 2, D, D, None) == ENULL
