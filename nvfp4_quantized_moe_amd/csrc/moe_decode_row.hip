@@ -1278,7 +1278,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1, 0, 0, 0);
                 }
                 if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
-                    // Token rows 0 of the quad sums (every A row holds the pair's h row).
+                    // Every A row holds the pair's h row: keep token 0 (q == 0)
+                    // of the quad sums.
                     const float oscale = exp2i(row_exp(bl->rmax[rl]));
                     const float s2 = bl->s2[rl];
                     const float g0 = moe::group_sum<4>(pick(acc0, c)) * oscale;
