@@ -546,6 +546,8 @@ def test_sort_fused_into_gate_up_matches_two_calls(T, k, E, H, I, mode):
     (2, 256, 512, 8, 3, "invalid"),     # ids outside [0, E) add nothing
     (5, 2048, 256, 64, 4, "rand"),      # two column groups per block
     (32, 2688, 1856, 128, 6, "zipf"),   # many tokens: four column groups, experts shared
+    (1, 256, 36736, 4, 1, "rand"),      # the widest h row the staging admits (k = 1)
+    (3, 512, 384, 6, 4, "null+invalid"),  # a NULL expert and an id outside [0, E) in one launch
 ])
 def test_down_blend_matches_down_then_blend(T, H, I, E, k, mode):
     """moe_nvfp4_down_blend against moe_nvfp4_down + moe_nvfp4_blend on the
@@ -567,6 +569,9 @@ def test_down_blend_matches_down_then_blend(T, H, I, E, k, mode):
             ids[1, 2] = E + 3
         elif mode == "null":
             nulls = (int(ids[0, 1]),)
+        elif mode == "null+invalid":
+            ids[2, 3] = -1
+            nulls = (int(ids[1, 0]),)
         case = Case(25, shape, ids=ids, weights=w, nulls=nulls)
     s, L = case.shape, case.layer
     case.run(fuse_blend=False)
