@@ -91,8 +91,10 @@ extern "C" {
  *   scale2[e]  the per-tensor f32 scale_2 (1.0 for plain MXFP4).
  * Weight element (n, k) = e2m1(nibble) * e4m3(scale of group k/16) * scale_2,
  * or, for K_MAJOR_MXFP4, e2m1(nibble) * e8m0(scale of group k/32) * scale_2.
- * packed[e] == NULL marks an absent expert (not owned under expert
- * parallelism): its rows of h and y are written as 0, so it contributes 0.
+ * packed[e] == NULL or scale[e] == NULL marks an absent expert (not owned
+ * under expert parallelism): its rows of h and y are written as 0, so it
+ * contributes 0.  The tables must hold at least E entries (the calls read
+ * entry e for every routed id e < E).
  * Scale codes must not be NaN (E4M3 0x7F, 0xFF; E8M0 0xFF): results are
  * then unspecified.  E8M0 codes above 252 can take a weight past the f32
  * range (it then decodes to infinity).

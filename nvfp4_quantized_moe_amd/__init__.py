@@ -161,31 +161,77 @@ def _out_ptr(out: torch.Tensor, numel: int) -> int:
     return _dev(out, torch.bfloat16, "out", numel)
 
 
+def _table_ptr(t, name: str, device) -> int:
+    """Address of an expert's weight tensor: contiguous uint8 on the table's device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name}: expected torch.uint8, got {t.dtype}")
+    if t.device.type != torch.device(device).type:
+        raise ValueError(f"{name}: on {t.device}, the table is built on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
 class ExpertTables:
     """One projection across E experts: device arrays of the experts' packed
     and scale pointers plus their f32 scale_2 values, in one of the layouts
     ROW_MAJOR, K_MAJOR (NVFP4) or K_MAJOR_MXFP4.  ``None`` in ``weights``
-    marks an absent (NULL) expert."""
+    marks an absent (NULL) expert; a present one is ``(packed, scale,
+    scale_2)`` with packed and scale contiguous uint8 device tensors.  The
+    element counts of every expert's tensors are kept so that each call can
+    check them against the (N, K) it is given (``check``) before any launch."""
 
     def __init__(self, weights: Sequence[Optional[tuple]], layout: int, device="cuda"):
-        packed, scales, s2 = [], [], []
+        if layout not in (ROW_MAJOR, K_MAJOR, K_MAJOR_MXFP4):
+            raise ValueError(f"ExpertTables: unknown layout {layout}")
+        packed, scales, s2, pn, sn = [], [], [], [], []
         self._keep = []
-        for w in weights:
+        for e, w in enumerate(weights):
             if w is None:
                 packed.append(0)
                 scales.append(0)
                 s2.append(0.0)
                 continue
             pk, sc, sv = w
-            packed.append(pk.data_ptr())
-            scales.append(sc.data_ptr())
+            if pk is None or sc is None:
+                raise ValueError(f"ExpertTables: expert {e} has a packed or scale tensor but not both "
+                                 "(pass None for an absent expert)")
+            packed.append(_table_ptr(pk, f"expert {e} packed", device))
+            scales.append(_table_ptr(sc, f"expert {e} scale", device))
             s2.append(float(sv))
+            pn.append(pk.numel())
+            sn.append(sc.numel())
             self._keep.append((pk, sc))
         self.packed = torch.tensor(packed, dtype=torch.int64, device=device)
         self.scale = torch.tensor(scales, dtype=torch.int64, device=device)
         self.scale2 = torch.tensor(s2, dtype=torch.float32, device=device)
         self.layout = int(layout)
         self.E = len(weights)
+        # Smallest packed / scale element count over the present experts.
+        self._min_packed = min(pn) if pn else None
+        self._min_scale = min(sn) if sn else None
+
+    @property
+    def group(self) -> int:
+        """k values per block scale: 32 for MXFP4, 16 for NVFP4."""
+        return 32 if self.layout == K_MAJOR_MXFP4 else 16
+
+    def check(self, name: str, E: int, n: int, k: int, pitch: int = 0) -> None:
+        """Raise ValueError unless the table covers E experts and every
+        present expert holds an [n, k] weight: n*k/2 packed bytes and
+        n*k/group scale bytes (a concatenated twin with row pitch ``pitch``:
+        k/2 * pitch and k/group * pitch)."""
+        if self.E < E:
+            raise ValueError(f"{name}: the table holds {self.E} experts, the call reads {E}")
+        if self._min_packed is None:
+            return
+        rows = pitch if pitch else n
+        need_p, need_s = (k // 2) * rows, (k // self.group) * rows
+        if self._min_packed < need_p or self._min_scale < need_s:
+            raise ValueError(f"{name}: an expert holds {self._min_packed} packed / {self._min_scale} scale "
+                             f"bytes, a [{n}, {k}] weight needs {need_p} / {need_s}")
 
     def abi(self) -> _Experts:
         return _Experts(self.packed.data_ptr(), self.scale.data_ptr(), self.scale2.data_ptr(), self.layout)
@@ -213,6 +259,8 @@ def moe_nvfp4_gate_up_silu(x, k, E, H, I, gate: ExpertTables, up: ExpertTables, 
                            sorted_token_ids, active_experts, active_count, h, stream=None) -> None:
     T = x.shape[0]
     P = T * k
+    gate.check("gate", E, I, H)
+    up.check("up", E, I, H)
     rc = lib().moe_nvfp4_gate_up_silu(
         _x_ptr(x, T * H), T, k, E, H, I, gate.abi(), up.abi(),
         _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
@@ -229,6 +277,8 @@ def moe_nvfp4_sort_gate_up_silu(topk_ids, x, E, H, I, gate: ExpertTables, up: Ex
     """Sort then gate+up (one launch in the few-token decode case); see the C header."""
     T, k = topk_ids.shape
     P = T * k
+    gate.check("gate", E, I, H)
+    up.check("up", E, I, H)
     rc = lib().moe_nvfp4_sort_gate_up_silu(
         _dev(topk_ids, torch.int32, "topk_ids"), _x_ptr(x, T * H),
         T, k, E, H, I, gate.abi(), up.abi(),
@@ -256,6 +306,7 @@ def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, e
     bytes apart, up columns from I on); see the C header."""
     T = x.shape[0]
     P = T * k
+    gate_up.check("gate_up", E, 2 * I, H, pitch=int(pitch))
     rc = lib().moe_nvfp4_gate_up_silu_concat(
         _x_ptr(x, T * H), T, k, E, H, I, gate_up.abi(), int(pitch),
         _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
@@ -269,6 +320,7 @@ def moe_nvfp4_gate_up_silu_concat(x, k, E, H, I, gate_up: ExpertTables, pitch, e
 def moe_nvfp4_down(h, T, k, E, H, I, down: ExpertTables, expert_offsets, active_experts, active_count,
                    y, stream=None) -> None:
     P = T * k
+    down.check("down", E, H, I)
     rc = lib().moe_nvfp4_down(
         _dev(h, torch.float32, "h", P * I), T, k, E, H, I, down.abi(),
         _dev(expert_offsets, torch.int32, "expert_offsets", E + 1),
@@ -290,6 +342,7 @@ def moe_nvfp4_blend(y, topk_weights, pair_pos, out, stream=None) -> None:
 def _down_blend_rc(h, topk_ids, topk_weights, pair_pos, E, H, I, down: ExpertTables, out, stream) -> int:
     T, k = topk_weights.shape
     P = T * k
+    down.check("down", E, H, I)
     return lib().moe_nvfp4_down_blend(
         _dev(h, torch.float32, "h", P * I), T, k, E, H, I, down.abi(),
         _dev(topk_ids, torch.int32, "topk_ids", P), _dev(topk_weights, torch.float32, "topk_weights"),

@@ -819,7 +819,7 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
     if (m0 >= rows) return;
     const int pr = min(a.pass_rows, rows - m0);
     constexpr int ucols = GATED ? 16 : 32;
-    if (pA == nullptr || pB == nullptr) {  // absent expert: its rows are zero
+    if (pA == nullptr || pB == nullptr || sA == nullptr || sB == nullptr) {  // absent expert: its rows are zero
         const int ncols = nu * ucols, n0 = u_first * ucols;
         for (int i = threadIdx.x; i < pr * ncols; i += kThreads) {
             const int m = i / ncols;
@@ -1145,7 +1145,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
             sa = a.sa[id];
             s2 = a.s2a[id];
         }
-        const bool live = routed && pa != nullptr;
+        const bool live = routed && pa != nullptr && sa != nullptr;
         const unsigned long long lm = __ballot(live);
         const int li = __popcll(lm & ((1ull << lane) - 1ull));
         if (live) {

@@ -8,10 +8,11 @@
 // sorted rows.
 //
 // gfx950 mapping:
-//   * v_mfma_f32_16x16x32_bf16: the activation rows are the A operand, the
-//     decoded weights the B operand, fp32 accumulation.  bf16 holds every
-//     E2M1 x E4M3 product exactly (at most 6 significant bits) and x as given;
-//     h is rounded to bf16 when staged for the down projection.
+//   * Matrix cores, fp32 accumulation: the activation rows are the A
+//     operand, the decoded weights the B operand.  Gate+up runs
+//     v_mfma_f32_16x16x32_bf16: bf16 holds every E2M1 x E4M3 (or E8M0)
+//     product exactly and x as given.  Down runs v_mfma_f32_16x16x32_f16
+//     with h as fp16 times a power of two per row (11 significant bits).
 //   * In the K-major layout one dword at packed row k/2 covers 4 adjacent
 //     columns x 2 k, so a lane holding the dwords of 4 consecutive packed rows
 //     holds 8 consecutive k of 4 columns: exactly the B operand (8 k of one
@@ -28,7 +29,7 @@
 //     with direct global-to-LDS loads three steps ahead, so no registers hold
 //     data in flight; each wave decodes its step's weights from LDS.
 //   * Down (k_gemm_down, up to 128 rows, 256 output columns per block):
-//     fp32 h is converted to bf16 in registers one step ahead; the weights
+//     fp32 h is converted to scaled fp16 in registers one step ahead; the weights
 //     stream through a register ring four steps deep, and the next step's
 //     weights are decoded between this step's MFMAs.
 //   * An expert's rows are split into balanced tiles.  Blocks are dealt to
@@ -108,20 +109,6 @@ __device__ __forceinline__ bf16x2_t decode_pair(uint32_t w, float sc) {
     else
         return __builtin_convertvector(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J) * sc, bf16x2_t);
 }
-template <bool MX>
-__device__ __forceinline__ void decode_pair_at(int u, const uint32_t (&w)[4], const Scales4 &sc, bf16x8_t (&b)[4]) {
-    const int r = u >> 2, j = u & 3;
-    bf16x2_t pr;
-    switch (j) {
-        case 0: pr = decode_pair<MX, 0>(w[r], sc.v[0]); break;
-        case 1: pr = decode_pair<MX, 1>(w[r], sc.v[1]); break;
-        case 2: pr = decode_pair<MX, 2>(w[r], sc.v[2]); break;
-        default: pr = decode_pair<MX, 3>(w[r], sc.v[3]); break;
-    }
-    b[j][2 * r] = pr.x;
-    b[j][2 * r + 1] = pr.y;
-}
-
 // All 4 packed rows of a step (8 consecutive k of columns 4c..4c+3) into the
 // B operands of the 4 interleaved column tiles.
 template <bool MX>
@@ -142,19 +129,6 @@ __device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf1
         b[3][2 * r] = p3.x;
         b[3][2 * r + 1] = p3.y;
     }
-}
-
-__device__ __forceinline__ u32x4_t f32x8_to_bf16x8(u32x4_t a, u32x4_t b) {
-    const f32x2_t v0 = {__uint_as_float(a.x), __uint_as_float(a.y)};
-    const f32x2_t v1 = {__uint_as_float(a.z), __uint_as_float(a.w)};
-    const f32x2_t v2 = {__uint_as_float(b.x), __uint_as_float(b.y)};
-    const f32x2_t v3 = {__uint_as_float(b.z), __uint_as_float(b.w)};
-    u32x4_t r;
-    r.x = moe::bitcast<uint32_t>(__builtin_convertvector(v0, bf16x2_t));
-    r.y = moe::bitcast<uint32_t>(__builtin_convertvector(v1, bf16x2_t));
-    r.z = moe::bitcast<uint32_t>(__builtin_convertvector(v2, bf16x2_t));
-    r.w = moe::bitcast<uint32_t>(__builtin_convertvector(v3, bf16x2_t));
-    return r;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory loads of this
@@ -313,15 +287,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Separate gate and up tables, or one concatenated twin whose up columns
     // start up_off bytes into each packed and scale row.
+    // An expert whose packed or scale pointer is NULL is absent.
     const uint8_t *pA = a.pa[e];
-    const uint8_t *pB = a.up_off ? (pA ? pA + a.up_off : nullptr) : a.pb[e];
-    if (pA == nullptr || pB == nullptr) {
+    const uint8_t *sA = a.sa[e];
+    const uint8_t *pB = a.up_off ? pA : a.pb[e];
+    const uint8_t *sB = a.up_off ? sA : a.sb[e];
+    if (pA == nullptr || pB == nullptr || sA == nullptr || sB == nullptr) {
         zero_rows(a, row0, mrows, n0, 128);
         return;
     }
     const bool up_wave = wave >= 2;
-    const uint8_t *pk = up_wave ? pB : pA;
-    const uint8_t *sk = up_wave ? (a.up_off ? a.sa[e] + a.up_off : a.sb[e]) : a.sa[e];
+    const uint8_t *pk = up_wave ? pB + a.up_off : pA;
+    const uint8_t *sk = up_wave ? sB + a.up_off : sA;
     const int ldb = a.ldb;
     const int n_ld = wact ? n_w : N - 64;  // idle waves (N not a multiple of 128) read valid columns
     const int S = K / kBK;
@@ -499,18 +476,137 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // ===========================================================================
 // Down.
+//
+// h (fp32) enters the matrix cores as fp16 times a power of two per row, the
+// weights as fp16: v_mfma_f32_16x16x32_f16 runs at the bf16 rate, and fp16
+// keeps 11 significant bits of h where bf16 keeps 8.
+//   * Row exponents.  h streams in 32-k steps, so a row's largest magnitude
+//     is not known when its first step is staged.  The exponent is set at
+//     the row's first nonzero step so that the step's maximum lands in
+//     [2^5, 2^6): every staged value then keeps 11 bits down to 2^-20 of
+//     that maximum, and a later step may be up to 2^9 times larger before
+//     it would reach 2^15.  If one is (the block's flag), the block runs
+//     again with each row's exponent taken from its exact maximum, read in
+//     a pass over the rows first; its first results are discarded.
+//   * Weights.  NVFP4: an E2M1 x E4M3 product is an fp16 number (at most 6
+//     significant bits, 2^-10 .. 2688): the fp4 converter, then one fp16
+//     multiply.  MXFP4: E8M0 spans more than fp16's range, so each output
+//     column is decoded relative to its largest scale code B (read once per
+//     block): the converter applies 2^(code + 13 - B), exact for codes down
+//     to B - 36 (a smaller one contributes under 2^-33 of the column's
+//     largest term and may round away), and the epilogue multiplies by
+//     2^(B - 140).  A column holding the NaN code 255 is NaN, as in the
+//     plain definition.
 // ===========================================================================
 constexpr int kRowsD = 128;                // rows per block tile
 constexpr int kMTD = kRowsD / 16;
-constexpr int kRowD = 80;                  // LDS bytes per staged row: 32 bf16 + 16 padding
+constexpr int kRowD = 80;                  // LDS bytes per staged row: 32 fp16 + 16 padding
 constexpr int kStageD = kRowsD * kRowD;
 constexpr int kChunksD = kRowsD * 4;       // 16-byte (8 k) chunks per step
 constexpr int kSlotsD = kChunksD / kThreads;
+constexpr int kExpFirst = 5;               // first nonzero step: its maximum lands in [2^5, 2^6)
+constexpr int kExpExact = 14;              // exact pass: the row maximum lands in [2^14, 2^15)
+constexpr int kExpLimit = 14;              // a staged maximum must stay below 2^(kExpLimit + 1)
+constexpr int kExpUnset = -1000;           // no nonzero value of the row seen yet
+constexpr int kMxBias = 127 + 13;          // MXFP4: f32 exponent field of 2^13 (6 * 2^13 < 65504)
 static_assert(kChunksD % kThreads == 0, "whole chunk slots");
+
+struct DownLds {
+    int efin[kRowsD];  // each row's exponent after the last step
+    int redo;          // nonzero: a step exceeded its row's range; run again with exact exponents
+};
+
+__device__ __forceinline__ float absmax8(const u32x4_t &a, const u32x4_t &b) {
+    const float u = fmaxf(fmaxf(fabsf(__uint_as_float(a.x)), fabsf(__uint_as_float(a.y))),
+                          fmaxf(fabsf(__uint_as_float(a.z)), fabsf(__uint_as_float(a.w))));
+    const float v = fmaxf(fmaxf(fabsf(__uint_as_float(b.x)), fabsf(__uint_as_float(b.y))),
+                          fmaxf(fabsf(__uint_as_float(b.z)), fabsf(__uint_as_float(b.w))));
+    return fmaxf(u, v);
+}
+
+// Largest magnitude over the quad of lanes holding one row's step (bits of
+// a non-negative float); the binade field of a nonzero maximum, subnormals
+// counted as the lowest normal binade, or 0 for an all-zero step.
+__device__ __forceinline__ int quad_binade(const u32x4_t &a, const u32x4_t &b) {
+    uint32_t m = __float_as_uint(absmax8(a, b));
+    m = max(m, moe::dpp_u32<moe::kDppXor1>(m));
+    m = max(m, moe::dpp_u32<moe::kDppXor2>(m));
+    return m == 0u ? 0 : max((int)(m >> 23), 1);
+}
+
+// 8 fp32 values times 2^e -> 8 fp16 (round to nearest even).
+__device__ __forceinline__ u32x4_t f32x8_to_f16x8(const u32x4_t &a, const u32x4_t &b, int e) {
+    auto pk = [e](uint32_t x, uint32_t y) {
+        const f32x2_t v = {__builtin_amdgcn_ldexpf(__uint_as_float(x), e), __builtin_amdgcn_ldexpf(__uint_as_float(y), e)};
+        return moe::bitcast<uint32_t>(__builtin_convertvector(v, f16x2_t));
+    };
+    u32x4_t r;
+    r.x = pk(a.x, a.y);
+    r.y = pk(a.z, a.w);
+    r.z = pk(b.x, b.y);
+    r.w = pk(b.z, b.w);
+    return r;
+}
+
+// fp16 scale operands of a step for the lane's 4 columns (bytes of a scale
+// dword): NVFP4, the E4M3 value in both halves; MXFP4, the f32 whose
+// exponent the converter applies, 2^(code + 13 - B), the field clamped to 1.
+struct ScalesH {
+    f16x2_t nv[4];
+    float mx[4];
+};
+template <bool MX>
+__device__ __forceinline__ ScalesH scales_h(uint32_t s, const int (&cbias)[4]) {
+    ScalesH r;
+    if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = (int)((s >> (8 * j)) & 0xffu) + cbias[j];
+            r.mx[j] = __uint_as_float((uint32_t)(f < 1 ? 1 : f) << 23);
+        }
+    } else {
+        const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
+        const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
+        r.nv[0] = f16x2_t{lo.x, lo.x};
+        r.nv[1] = f16x2_t{lo.y, lo.y};
+        r.nv[2] = f16x2_t{hi.x, hi.x};
+        r.nv[3] = f16x2_t{hi.y, hi.y};
+    }
+    return r;
+}
+
+template <bool MX, int J>
+__device__ __forceinline__ f16x2_t decode_pair_h(uint32_t w, const ScalesH &sc) {
+    if constexpr (MX)
+        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.mx[J], J);
+    else
+        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, J) * sc.nv[J];
+}
+// Element pair u = 4r + j (packed row r, column 4c + j) into the B operands.
+template <bool MX>
+__device__ __forceinline__ void decode_pair_h_at(int u, const uint32_t (&w)[4], const ScalesH &sc,
+                                                 f16x8_t (&b)[4]) {
+    const int r = u >> 2, j = u & 3;
+    f16x2_t pr;
+    switch (j) {
+        case 0: pr = decode_pair_h<MX, 0>(w[r], sc); break;
+        case 1: pr = decode_pair_h<MX, 1>(w[r], sc); break;
+        case 2: pr = decode_pair_h<MX, 2>(w[r], sc); break;
+        default: pr = decode_pair_h<MX, 3>(w[r], sc); break;
+    }
+    b[j][2 * r] = pr.x;
+    b[j][2 * r + 1] = pr.y;
+}
+template <bool MX>
+__device__ __forceinline__ void decode_b_h(const uint32_t (&w)[4], const ScalesH &sc, f16x8_t (&b)[4]) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) decode_pair_h_at<MX>(u, w, sc, b);
+}
 
 template <bool MX>  // MXFP4 weights (E8M0 scales per 32 k) instead of NVFP4
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_down(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageD];
+    __shared__ __attribute__((aligned(16))) DownLds bk;
 
     Unit un;
     if (!find_unit<kRowsD>(a, un)) return;  // uniform exit
@@ -525,11 +621,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const size_t row0 = (size_t)un.lo + un.m0;
 
     const uint8_t *pk = a.pa[e];
-    if (pk == nullptr) {
+    const uint8_t *sk = a.sa[e];
+    if (pk == nullptr || sk == nullptr) {
         zero_rows(a, row0, mrows, n0, 256);
         return;
     }
-    const uint8_t *sk = a.sa[e];
     const int n_ld = wact ? n_w : N - 64;
     // Per-lane byte offsets (32-bit) from wave-uniform bases.
     const int ldb = a.ldb;
@@ -540,20 +636,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int S = K / kBK;
     const int mt_used = (mrows + 15) >> 4;
 
-    // ---- activations: fp32 h rows -> bf16, register staging one step ahead.
+    if (tid == 0) bk.redo = 0;
+
+    // MXFP4: the largest scale code B of each of the lane's 4 columns (the 4
+    // lanes sharing them read every fourth scale row), kept as kMxBias - B.
+    int cbias[4] = {0, 0, 0, 0};
+    if constexpr (MX) {
+        uint32_t m[4] = {0u, 0u, 0u, 0u};
+        for (int r = q; r < S; r += 4) {
+            const uint32_t d = gload<uint32_t>(sk + (size_t)r * ldb + n_ld + 4 * c);
+            m[0] = max(m[0], d & 0xffu);
+            m[1] = max(m[1], (d >> 8) & 0xffu);
+            m[2] = max(m[2], (d >> 16) & 0xffu);
+            m[3] = max(m[3], d >> 24);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 16, 64));
+            m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 32, 64));
+            cbias[j] = kMxBias - (int)m[j];
+        }
+    }
+
+    // ---- activations: fp32 h rows -> fp16 times 2^E(row), register staging
+    // one step ahead.  Thread t stages octet t % 4 of rows t / 4 and
+    // t / 4 + 64, so a row's 4 octets sit in one quad of lanes, each of which
+    // keeps the row's exponent.
     const uint8_t *hbytes = static_cast<const uint8_t *>(a.act);
+    const int srow = tid >> 2, soct = tid & 3;
     uint32_t aoff[kSlotsD];
-    int adst[kSlotsD];
 #pragma unroll
     for (int j = 0; j < kSlotsD; ++j) {
-        const int ch = tid + kThreads * j;
-        const int row = ch >> 2, oct = ch & 3;
+        const int row = srow + (kThreads / 4) * j;
         const int rr = row < mrows ? row : 0;
-        aoff[j] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8 * oct) * 4u;  // h below 4 GiB
-        adst[j] = row * kRowD + 16 * oct;
+        aoff[j] = ((uint32_t)(row0 + rr) * (uint32_t)K + 8 * soct) * 4u;  // h below 4 GiB
     }
+    int ecur[kSlotsD];
     u32x4_t ar[kSlotsD][2];
-    auto load_a = [&](int s) {
+    auto load_a = [&](int s) __attribute__((always_inline)) {
         const uint8_t *base = hbytes + (size_t)s * kBK * 4;
 #pragma unroll
         for (int j = 0; j < kSlotsD; ++j) {
@@ -561,16 +681,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             ar[j][1] = gload<u32x4_t>(base + aoff[j] + 16);
         }
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int buf) __attribute__((always_inline)) {
+        bool over = false;
 #pragma unroll
-        for (int j = 0; j < kSlotsD; ++j)
-            *reinterpret_cast<u32x4_t *>(lds + buf * kStageD + adst[j]) = f32x8_to_bf16x8(ar[j][0], ar[j][1]);
+        for (int j = 0; j < kSlotsD; ++j) {
+            const int fe = quad_binade(ar[j][0], ar[j][1]);
+            if (fe != 0 && ecur[j] == kExpUnset) ecur[j] = kExpFirst + 127 - fe;  // the accumulators are still zero
+            over |= fe + ecur[j] > 127 + kExpLimit;
+            *reinterpret_cast<u32x4_t *>(lds + buf * kStageD + (srow + (kThreads / 4) * j) * kRowD + 16 * soct) =
+                f32x8_to_f16x8(ar[j][0], ar[j][1], ecur[j]);
+        }
+        if (over) bk.redo = 1;
     };
 
     // ---- weight ring in registers ---------------------------------------
     uint32_t bw[kBDist][4];
     uint32_t bs[kBDist];
-    auto load_b = [&](int slot_s, uint32_t (&w)[4], uint32_t &sv) {
+    auto load_b = [&](int slot_s, uint32_t (&w)[4], uint32_t &sv) __attribute__((always_inline)) {
         const int s = slot_s < S ? slot_s : S - 1;
         const uint8_t *p = pk + (size_t)(16 * s) * ldb;
 #pragma unroll
@@ -579,53 +706,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     f32x4_t acc[kMTD][4];
-#pragma unroll
-    for (int i = 0; i < kMTD; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // B operands of the current step and of the next one (decoded while the
-    // current step's MFMAs run).
-    bf16x8_t bop[2][4];
-#pragma unroll
-    for (int d = 0; d < kBDist; ++d) load_b(d, bw[d], bs[d]);
-    load_a(0);
-    store_a(0);
-    decode_b<MX>(bw[0], bs[0], bop[0]);
-    load_b(kBDist, bw[0], bs[0]);
-    __syncthreads();
-
+    f16x8_t bop[2][4];  // B operands of the current step and of the next one
     const uint8_t *abase = lds + c * kRowD + 16 * q;
 
     // Step s: ring slot s % kBDist was decoded into bop[s % 2] during step
     // s - 1; this step decodes step s + 1 and refills its slot with step
     // s + 1 + kBDist (unconditionally, clamped: the compiler then keeps the
     // ring in flight across iterations).  Every row tile runs.
-    auto step = [&](int s, auto slot) {
+    auto step = [&](int s, auto slot) __attribute__((always_inline)) {
         constexpr int d = decltype(slot)::value;
         constexpr int p = d & 1;
         constexpr int dn = (d + 1) % kBDist;
         const bool more = s + 1 < S;
         if (more) load_a(s + 1);
         const uint8_t *ab = abase + p * kStageD;
-        const Scales4 scn = scales4<MX>(bs[dn]);
+        const ScalesH scn = scales_h<MX>(bs[dn], cbias);
         // Hand-ordered: row-tile operands are read two tiles ahead, and one
-        // element pair of the next step's decode (4 VALU) follows every other
-        // MFMA.  Full scheduling fences keep this order; the empty asm after
-        // each decoded pair pins it there (otherwise it is sunk to its use in
-        // the next step).
-        bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(ab);
-        bf16x8_t an = *reinterpret_cast<const bf16x8_t *>(ab + 16 * kRowD);
+        // element pair of the next step's decode follows every other MFMA.
+        // Full scheduling fences keep this order; the empty asm after each
+        // decoded pair pins it there (otherwise it is sunk to its use in the
+        // next step).
+        f16x8_t av = *reinterpret_cast<const f16x8_t *>(ab);
+        f16x8_t an = *reinterpret_cast<const f16x8_t *>(ab + 16 * kRowD);
 #pragma unroll
         for (int i = 0; i < kMTD; ++i) {
-            const bf16x8_t an2 = *reinterpret_cast<const bf16x8_t *>(ab + (i + 2 < kMTD ? i + 2 : kMTD - 1) * 16 * kRowD);
+            const f16x8_t an2 = *reinterpret_cast<const f16x8_t *>(ab + (i + 2 < kMTD ? i + 2 : kMTD - 1) * 16 * kRowD);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[p][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bop[p][j], acc[i][j], 0, 0, 0);
                 const int m = 4 * i + j;  // MFMA index in the step
                 if ((m & 1) == 0 && m / 2 < 16) {
-                    decode_pair_at<MX>(m / 2, bw[dn], scn, bop[p ^ 1]);
+                    decode_pair_h_at<MX>(m / 2, bw[dn], scn, bop[p ^ 1]);
                     asm volatile("" : "+v"(bop[p ^ 1][0]), "+v"(bop[p ^ 1][1]), "+v"(bop[p ^ 1][2]), "+v"(bop[p ^ 1][3]));
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -637,30 +749,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (more) store_a(p ^ 1);
         __syncthreads();
     };
-    int s0 = 0;
-    for (; s0 + kBDist <= S; s0 += kBDist) {
-        step(s0 + 0, I0{});
-        step(s0 + 1, I1{});
-        step(s0 + 2, I2{});
-        step(s0 + 3, I3{});
-    }
-    if (s0 + 0 < S) step(s0 + 0, I0{});
-    if (s0 + 1 < S) step(s0 + 1, I1{});
-    if (s0 + 2 < S) step(s0 + 2, I2{});
 
-    // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j] ----
+    // The pipeline: each row's exponent from its first nonzero step (exact =
+    // false) or from the rows' exact maxima, read in a pass first (exact =
+    // true: used when a later step of some row exceeded its range).
+    auto run = [&](bool exact) __attribute__((always_inline)) {
+        if (!exact) {
+#pragma unroll
+            for (int j = 0; j < kSlotsD; ++j) ecur[j] = kExpUnset;
+        } else {
+            int fmax[kSlotsD];
+#pragma unroll
+            for (int j = 0; j < kSlotsD; ++j) fmax[j] = 0;
+            for (int s = 0; s < S; ++s) {
+                load_a(s);
+#pragma unroll
+                for (int j = 0; j < kSlotsD; ++j) fmax[j] = max(fmax[j], quad_binade(ar[j][0], ar[j][1]));
+            }
+#pragma unroll
+            for (int j = 0; j < kSlotsD; ++j) ecur[j] = fmax[j] == 0 ? kExpUnset : kExpExact + 127 - fmax[j];
+        }
+#pragma unroll
+        for (int i = 0; i < kMTD; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < kBDist; ++d) load_b(d, bw[d], bs[d]);
+        load_a(0);
+        __syncthreads();  // the redo flag is cleared; earlier readers of the stage buffers are done
+        store_a(0);
+        decode_b_h<MX>(bw[0], scales_h<MX>(bs[0], cbias), bop[0]);
+        load_b(kBDist, bw[0], bs[0]);
+        __syncthreads();
+
+        int s0 = 0;
+        for (; s0 + kBDist <= S; s0 += kBDist) {
+            step(s0 + 0, I0{});
+            step(s0 + 1, I1{});
+            step(s0 + 2, I2{});
+            step(s0 + 3, I3{});
+        }
+        if (s0 + 0 < S) step(s0 + 0, I0{});
+        if (s0 + 1 < S) step(s0 + 1, I1{});
+        if (s0 + 2 < S) step(s0 + 2, I2{});
+    };
+    run(false);
+    // The last barrier follows every store_a, so the flag is final.  Exact
+    // exponents cannot exceed the range: a second run always completes.
+    if (__builtin_amdgcn_readfirstlane(bk.redo) != 0) run(true);
+
+    // ---- epilogue: acc[i][j][v] = C[row 16i + 4q + v][column n_w + 4c + j],
+    // scaled by 2^-E(row) (and 2^(B - 140) per MXFP4 column).
+    if (soct == 0) {
+#pragma unroll
+        for (int j = 0; j < kSlotsD; ++j) bk.efin[srow + (kThreads / 4) * j] = ecur[j];
+    }
+    __syncthreads();
     if (!wact) return;
     const float s2 = a.s2a[e];
 #pragma unroll
     for (int i = 0; i < kMTD; ++i) {
         if (i < mt_used) {
+            const int4 ev = *reinterpret_cast<const int4 *>(&bk.efin[16 * i + 4 * q]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 16 * i + 4 * q + v;
                 if (row < mrows) {
-                    const float4 o = make_float4(acc[i][0][v] * s2, acc[i][1][v] * s2, acc[i][2][v] * s2,
-                                                 acc[i][3][v] * s2);
-                    *reinterpret_cast<float4 *>(a.out + (row0 + row) * N + n_w + 4 * c) = o;
+                    const int er = v == 0 ? ev.x : (v == 1 ? ev.y : (v == 2 ? ev.z : ev.w));
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        o[j] = __builtin_amdgcn_ldexpf(acc[i][j][v], -er - cbias[j]) * s2;
+                        if constexpr (MX) o[j] = cbias[j] == kMxBias - 255 ? __builtin_nanf("") : o[j];
+                    }
+                    *reinterpret_cast<float4 *>(a.out + (row0 + row) * N + n_w + 4 * c) =
+                        make_float4(o[0], o[1], o[2], o[3]);
                 }
             }
         }

@@ -115,8 +115,62 @@ def test_python_binding_checks_buffer_sizes():
 class _Table:
     """Stands in for an ExpertTables where only the argument checks run."""
 
+    def check(self, *args, **kwargs):
+        pass
+
     def abi(self):
         return _ex()
+
+
+def _cpu_tables(n, k, E, layout=moe.ROW_MAJOR, short=None, missing_scale=None):
+    """ExpertTables over CPU tensors (only the host-side checks look at them):
+    E experts of [n, k]; expert ``short`` one scale byte short."""
+    import torch
+
+    g = 32 if layout == moe.K_MAJOR_MXFP4 else 16
+    rows = []
+    for e in range(E):
+        pk = torch.zeros(n * k // 2, dtype=torch.uint8)
+        sc = torch.zeros(n * k // g - (1 if e == short else 0), dtype=torch.uint8)
+        rows.append((pk, None if e == missing_scale else sc, 1.0))
+    return moe.ExpertTables(rows, layout, device="cpu")
+
+
+def test_expert_tables_checked_against_the_call():
+    """Tables shorter than E, or an expert smaller than the [N, K] weight
+    the call reads, are refused before any launch; an expert with packed
+    bytes but no scales is refused when the table is built."""
+    import torch
+
+    i32 = dict(dtype=torch.int32)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    args = (torch.zeros(5, **i32), torch.zeros(8, **i32), torch.zeros(4, **i32), torch.zeros(1, **i32),
+            torch.zeros((8, 512)))
+    good = _cpu_tables(512, 256, 4)
+    with pytest.raises(ValueError, match="holds 3 experts, the call reads 4"):
+        moe.moe_nvfp4_gate_up_silu(x, 2, 4, 256, 512, _cpu_tables(512, 256, 3), good, *args)
+    with pytest.raises(ValueError, match="up: an expert holds"):
+        moe.moe_nvfp4_gate_up_silu(x, 2, 4, 256, 512, good, _cpu_tables(512, 256, 4, short=2), *args)
+    with pytest.raises(ValueError, match="down: an expert holds"):
+        moe.moe_nvfp4_down(torch.zeros((8, 512)), 4, 2, 4, 256, 512, _cpu_tables(256, 512, 4, short=0),
+                           *args[:1], *args[2:4], torch.zeros((8, 256)))
+    with pytest.raises(ValueError, match="down: an expert holds"):   # MXFP4 scale group of 32
+        moe.moe_nvfp4_down(torch.zeros((8, 512)), 4, 2, 4, 256, 512,
+                           _cpu_tables(256, 512, 4, moe.K_MAJOR_MXFP4, short=3), *args[:1], *args[2:4],
+                           torch.zeros((8, 256)))
+    with pytest.raises(ValueError, match="packed or scale tensor but not both"):
+        _cpu_tables(512, 256, 4, missing_scale=1)
+    with pytest.raises(TypeError, match="uint8"):
+        moe.ExpertTables([(torch.zeros(8, dtype=torch.int32), torch.zeros(8, dtype=torch.uint8), 1.0)],
+                         moe.ROW_MAJOR, device="cpu")
+    # the right sizes pass the table checks (and then stop at the CPU tensors)
+    with pytest.raises(ValueError, match="expected a device tensor"):
+        moe.moe_nvfp4_gate_up_silu(x, 2, 4, 256, 512, good, good, *args)
+    # a concatenated twin is checked against its row pitch
+    cc = moe.ExpertTables([(torch.zeros(128 * 1040, dtype=torch.uint8), torch.zeros(16 * 1040, dtype=torch.uint8),
+                            1.0)] * 4, moe.K_MAJOR, device="cpu")
+    with pytest.raises(ValueError, match="gate_up: an expert holds"):
+        moe.moe_nvfp4_gate_up_silu_concat(x, 2, 4, 256, 512, cc, 1056, *args)
 
 
 def test_route_rejects():

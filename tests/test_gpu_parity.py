@@ -638,15 +638,56 @@ def test_layer_graph_replays_match_eager():
 
 
 # ---------------------------------------------------------------- widest admitted rows
-@pytest.mark.parametrize("kmajor,H", [(False, 36736), (True, 65536)])
-def test_widest_hidden_width(kmajor, H):
+@pytest.mark.parametrize("kmajor,H,I", [(False, 36736, 256), (True, 65536, 64)])
+def test_widest_hidden_width(kmajor, H, I):
     """The widest activation rows each path admits: the decode kernel stages
-    one row of x (fp16) in its LDS budget, so K = H <= 36736; the K-major GEMM
-    takes the full MOE_NVFP4_MAX_WIDTH = 65536.  (I = 256: with a 64-wide
-    down projection and 393K outputs, the tail of the bf16 rounding of h
-    before the K-major down GEMM reaches 1.11 of the strict bound, the
-    official one holding at 0.006; 64-wide down projections are covered at
-    fewer outputs by the ragged MXFP4 shapes.)"""
-    say("widest H", H, "kmajor" if kmajor else "row")
-    shape = synth.MoeShape(f"wide_h_{H}", 6, H, 256, 2, 1, "uniform", kmajor)
+    one row of x (fp16) in its LDS budget, so K = H <= 36736 (and I >= 256
+    on that path); the K-major GEMM takes the full MOE_NVFP4_MAX_WIDTH =
+    65536, here with the narrowest down projection it admits (I = 64):
+    393K outputs, each a sum of 64 products of h rounded to fp16."""
+    say("widest H", H, "I", I, "kmajor" if kmajor else "row")
+    shape = synth.MoeShape(f"wide_h_{H}", 6, H, I, 2, 1, "uniform", kmajor)
     _full_check(Case(25, shape), f"widest H {H}")
+
+
+# ---------------------------------------------------------------- K-major down: row exponents of h
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_kmajor_down_row_exponents(fmt):
+    """The K-major down projection stages h as fp16 with one power of two per
+    row, set at the row's first nonzero 32-k step.  Crafted h rows: a first
+    step 2^-12 of the rest and a tail grown by 2^20 (a later step exceeds
+    the first step's range, so the block runs again with exact exponents),
+    zeros up to k = 200, all zeros, and rows at 2^60 and 2^-60.  Each y row
+    is compared with the oracle at its own magnitude; zero rows give zero."""
+    say("K-major down row exponents", fmt)
+    shape = synth.MoeShape(f"down_rows_{fmt}", 40, 512, 384, 2, 2, "uniform", True)
+    case = Case(27, shape, fmt=fmt)
+    case.run()  # the sort outputs the down launch indexes with
+    L, P, I = case.layer, shape.P, shape.I
+    h = np.random.default_rng(27).standard_normal((P, I))
+    h[0::7, :32] *= 2.0 ** -12
+    h[1::7, :200] = 0.0
+    h[2::7, :] = 0.0
+    h[3::7] *= 2.0 ** 60
+    h[4::7] *= 2.0 ** -60
+    h[5::7, 300:] *= 2.0 ** 20
+    h32 = h.astype(np.float32)
+    L.h.copy_(torch.from_numpy(h32).cuda())
+    L.y.fill_(7.0)
+    moe.moe_nvfp4_down(L.h, shape.T, shape.k, shape.E, shape.H, shape.I, L.down, L.expert_offsets,
+                       L.active_experts, L.active_count, L.y)
+    torch.cuda.synchronize()
+    y = _h2f(L.y)
+    offs = L.expert_offsets.cpu().numpy()
+    wf = case.weight_fn()
+    for e in range(shape.E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi == lo:
+            continue
+        Wd = oracle.expert_weights(wf, e, shape.H, shape.I, False, fmt)[2]
+        y_ref = oracle.down_rows(h32[lo:hi].astype(np.float64), Wd)
+        for p in range(lo, hi):
+            if not h32[p].any():
+                assert not y[p].any(), p
+                continue
+            parity.assert_parity_relative(y[p], y_ref[p - lo], f"{fmt} y row {p}")
