@@ -1,38 +1,51 @@
 """Benchmark of the grouped NVFP4 MoE expert projection on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--eager] [--format nvfp4|mxfp4]
+    python bench.py [--steps K] [--warmup W] [--workload N] [--eager] [--format nvfp4|mxfp4]
                     [--gate-up separate|concat]
 
 A step is one MoE layer forward through the whole path — routing sort,
 gate+up+SiLU, down, blend — over one batch of synthetic input (at one
 token the sort runs inside the gate+up launch and the blend inside the down
-launch).  Every input
-is resident in HBM before timing starts.  Consecutive steps run different
-layers' expert weights (separate HBM copies, as successive layers of a model
-would), so the weights a step reads were last touched far more than the
-256 MB Infinity Cache ago: the measured bandwidth is HBM bandwidth.
+launch).  Every input is resident in HBM before timing starts.  Consecutive
+steps run different layers' expert weights (separate HBM copies, as
+successive layers of a model would), so the weights a step reads were last
+touched far more than the 256 MB Infinity Cache ago: the measured bandwidth
+is HBM bandwidth.
 
-The K timed steps are captured into one HIP graph and replayed once, between
-a device synchronisation on each side (``--eager`` launches them one by one
-instead).  Reported on one JSON line:
+With no --workload the line covers both halves of the metric: the 1-token
+decode workload (the top-level fields) and the 32-token decode workload
+(the ``decode_batch_32`` block, same fields).  --workload N measures that
+workload alone.
+
+The K timed steps are captured into one HIP graph.  It is replayed once
+untimed (the first replay of a graph also uploads it), then a 1 GiB buffer
+is rewritten to evict the caches, then the timed replay runs between a
+device synchronisation on each side (``--eager`` launches the steps one by
+one instead).  A one-wave spin kernel of about a millisecond runs just ahead
+of the start event, so that the host has submitted the replay before the
+timed region opens (otherwise a fixed submission latency of the order of
+50 us lands in it, a few percent of a 20-step replay).  Reported on one JSON line, per workload:
   value       expert-weight bytes of the active experts per step / step time (GB/s)
   tokens_per_s, pct_of_hbm_peak
+  dtype       the arithmetic: f16 (decode: fp16 matrix-core operands, fp32
+              accumulation) or bf16/f16 (many-token: bf16 gate+up, fp16 down)
   roofline    the dominant kernel (gate+up+SiLU, with the routing sort fused
               in where the step runs it that way: one token): its
               algorithmic bytes per launch / its mean launch duration, timed
-              with HIP events on the
-              stream it runs on, against 8 TB/s (the many-token K-major
-              workload: its flops per launch against the 2.5 PFLOP/s bf16/fp16
-              matrix-core peak); traffic = HBM bytes per launch from the
-              committed counter summary in profiles/ while the kernel sources
-              are unchanged since it was taken, else null
-  --format mxfp4 runs the many-token workload with MXFP4 experts (E8M0
-  scales per 32 k) instead of NVFP4; --gate-up concat runs its gate+up over
-  one concatenated gate||up twin per expert; the workload name says so.
+              with HIP events on the stream it runs on, against 8 TB/s (the
+              many-token K-major workload: its flops per launch against the
+              2.5 PFLOP/s fp16/bf16 matrix-core peak); traffic = HBM bytes per
+              launch from the committed counter summary in profiles/ while
+              the kernel sources are unchanged since it was taken, else null
   router      launch time of moe_nvfp4_route on the workload's logits (the
               router ahead of the path; not part of the step)
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
               same workload, in the same unit
+  cpu_oracle_1thread (top level) the oracle with BLAS held to one thread on
+              one forward of each of the tiny, 1-token and 32-token workloads
+  --format mxfp4 runs the many-token workload with MXFP4 experts (E8M0
+  scales per 32 k) instead of NVFP4; --gate-up concat runs its gate+up over
+  one concatenated gate||up twin per expert; the workload name says so.
 """
 from __future__ import annotations
 
@@ -49,6 +62,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
 METRIC = "expert-weight HBM GB/s (% of peak) + MoE-layer tokens/s, decode batch 1/32"
+SPIN_CYCLES = 2_500_000  # a one-wave spin of about 1 ms ahead of each timed region
 
 
 def parse():
@@ -56,7 +70,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", type=int, default=2, help="workload id 1..5 (2 = decode, 1 token)")
+    ap.add_argument("--workload", type=int, default=None,
+                    help="workload id 1..5 (default: 2, the 1-token decode, with 3, the 32-token decode, as a block)")
     ap.add_argument("--layers", type=int, default=0, help="weight copies cycled over (0 = auto)")
     ap.add_argument("--batches", type=int, default=8, help="distinct routing batches cycled over")
     ap.add_argument("--eager", action="store_true", help="launch step by step instead of one graph")
@@ -66,9 +81,10 @@ def parse():
                     help="gate and up as two K-major twins, or one concatenated twin (K-major workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--profile-pass", choices=["gate_up", "copy"], default=None,
-                    help="for counter runs under rocprofv3: launch only gate+up+SiLU (after one sort) "
-                         "--steps times, or a plain 1 GiB device copy --steps times, then exit")
+    ap.add_argument("--profile-pass", choices=["gate_up", "down", "copy"], default=None,
+                    help="for counter runs under rocprofv3: launch only gate+up+SiLU (after one sort), or "
+                         "only the down projection (after one sort and gate+up), --steps times, or a plain "
+                         "1 GiB device copy --steps times, then exit")
     return ap.parse_args()
 
 
@@ -187,22 +203,50 @@ def cpu_baseline(shape, cfg_id, seconds, fmt="nvfp4"):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def cpu_oracle_1thread():
+    """The oracle with BLAS held to one thread (numpy's elementwise work is
+    single-threaded anyway): one layer forward of each of the tiny, 1-token
+    and 32-token decode workloads, weights generated outside the timing."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
 
+    res = {}
+    with threadpool_limits(limits=1):
+        for cfg_id in (1, 2, 3):
+            shape = synth.config(cfg_id)
+            x = synth.gen_x(cfg_id, shape)
+            ids, w = synth.gen_routing(cfg_id, shape)
+            cache = {(int(e), p): (*synth.gen_expert(cfg_id, int(e), p, shape), synth.SCALE2_F32)
+                     for e in np.unique(ids) for p in (0, 1, 2)}
+            t0 = time.perf_counter()
+            oracle.moe_layer(x, ids, w, lambda e, p: cache[(e, p)], shape.E, shape.H, shape.I)
+            dt = time.perf_counter() - t0
+            res[shape.name] = {"seconds_per_forward": round(dt, 3),
+                               "value": round(active_weight_bytes(shape, ids) / dt / 1e9, 4), "unit": "GB/s",
+                               "tokens_per_s": round(shape.T / dt, 3), "cores": 1}
+    return res
+
+
+def flush_caches(dev, scratch=[]):
+    """Rewrite a 1 GiB device buffer (more than the 256 MB Infinity Cache and
+    the L2s together), so the next step finds nothing of its weights cached."""
+    import torch
+
+    if not scratch:
+        scratch.append(torch.empty(1 << 30, dtype=torch.uint8, device=dev))
+    scratch[0].fill_(1)
+
+
+def measure(args, cfg_id, K, W):
+    """One workload: build its inputs and weight copies, time K steps, and
+    return its fields of the JSON line."""
     import torch
 
     import nvfp4_quantized_moe_amd as moe
     import synth
 
-    if not torch.cuda.is_available():
-        sys.exit("bench.py: no GPU")
-    moe.lib()  # fail loudly when the HIP library is missing
     dev = torch.device("cuda:0")
-    cfg_id = args.workload
     shape = synth.config(cfg_id)
     mx = args.format == "mxfp4"
     if mx and not shape.kmajor:
@@ -286,8 +330,12 @@ def main():
             moe.moe_nvfp4_gate_up_silu(xs[0], shape.k, shape.E, shape.H, shape.I, tabs[0], tabs[1],
                                        bufs.expert_offsets, bufs.sorted_token_ids, bufs.active_experts,
                                        bufs.active_count, bufs.h, s)
-    torch.cuda.synchronize()
 
+    def sort_launch(s):
+        moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
+                           bufs.active_experts, bufs.active_count, bufs.err_flag, s)
+
+    torch.cuda.synchronize()
     stream = torch.cuda.Stream()
 
     if args.profile_pass == "copy":
@@ -297,15 +345,21 @@ def main():
             for _ in range(args.steps):
                 dst.copy_(src)
         torch.cuda.synchronize()
-        return
-    if args.profile_pass == "gate_up":
+        return None
+    if args.profile_pass in ("gate_up", "down"):
         with torch.cuda.stream(stream):
-            moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
-                               bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
+            sort_launch(stream)
+            if args.profile_pass == "down":
+                gate_up_launch(0, stream)
             for i in range(args.steps):
-                gate_up_launch(i, stream)
+                if args.profile_pass == "gate_up":
+                    gate_up_launch(i, stream)
+                else:
+                    dn = layers[i % L][1][2]
+                    moe.moe_nvfp4_down(bufs.h, shape.T, shape.k, shape.E, shape.H, shape.I, dn,
+                                       bufs.expert_offsets, bufs.active_experts, bufs.active_count, bufs.y, stream)
         torch.cuda.synchronize()
-        return
+        return None
 
     def step(i, s):
         bufs.gate, bufs.up, bufs.down = layers[i % L][1]
@@ -317,7 +371,6 @@ def main():
         for i in range(first, first + n):
             step(i, s)
 
-    K, W = args.steps, args.warmup
     with torch.cuda.stream(stream):
         run_steps(0, min(W, 3), stream)  # plain warm launch before any capture
     torch.cuda.synchronize()
@@ -326,12 +379,18 @@ def main():
     if args.eager:
         with torch.cuda.stream(stream):
             run_steps(0, W, stream)
-            torch.cuda.synchronize()
+        flush_caches(dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(SPIN_CYCLES)
             t_start.record(stream)
             run_steps(W, K, stream)
             t_end.record(stream)
         torch.cuda.synchronize()
     else:
+        # Warm-up steps run as their own graph; the timed graph is replayed
+        # once untimed (its first replay uploads it), the caches are flushed,
+        # and its next replay is timed.
         g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_warm, stream=stream):
             run_steps(0, max(W, 1), stream)
@@ -339,8 +398,15 @@ def main():
             run_steps(W, K, stream)
         torch.cuda.synchronize()
         g_warm.replay()
+        g_main.replay()
+        torch.cuda.synchronize()
+        flush_caches(dev)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
+            # The GPU spins for about a millisecond ahead of the timed region
+            # while the host submits the graph, so the timed region holds the
+            # K steps and not the submission latency of the replay.
+            torch.cuda._sleep(SPIN_CYCLES)
             t_start.record(stream)
             g_main.replay()
             t_end.record(stream)
@@ -355,11 +421,10 @@ def main():
     # stream it runs on bracket Kr back-to-back launches (one routing batch,
     # the weight copies cycled as in the timed steps); the mean per launch
     # includes the short gap between consecutive launches.
-    Kr = min(K, 200)
+    Kr = min(max(K, 50), 200)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        moe.moe_nvfp4_sort(ids_d[0], shape.E, bufs.expert_offsets, bufs.sorted_token_ids, bufs.pair_pos,
-                           bufs.active_experts, bufs.active_count, bufs.err_flag, stream)
+        sort_launch(stream)
         for rep in range(2):  # the first pass warms the launch path
             e0.record(stream)
             for i in range(Kr):
@@ -370,7 +435,7 @@ def main():
     gu_bytes = float(gate_up_bytes(shape, idss[0], group)) + (shape.P * 4 if fused_sort else 0)
     traffic = measured_traffic(shape.name)
     if shape.kmajor:
-        # Many-token path: a dense bf16 contraction on the matrix cores.
+        # Many-token path: a dense contraction on the matrix cores.
         flops = 4.0 * shape.P * shape.I * shape.H  # gate and up, 2 flops per MAC
         roof = {"bound": "mfma", "achieved": round(flops / (gu_ms / 1e3) / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
@@ -400,20 +465,12 @@ def main():
     router = {"kernel": "moe_nvfp4_route", "launch_us": round(e0.elapsed_time(e1) / Kq * 1e3, 3),
               "in_step": False}
 
-
-    line = {
-        "metric": METRIC,
+    block = {
         "value": round(value, 2),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+        "dtype": "bf16/f16" if shape.kmajor else "f16",
+        "accumulate": "f32",
         "config": {
             "workload": shape.name,
             "tokens": shape.T, "hidden": shape.H, "expert_inter": shape.I, "experts": shape.E, "top_k": shape.k,
@@ -429,8 +486,40 @@ def main():
         "router": router,
         "cpu_baseline": None,
     }
+    del layers, base, bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(shape, cfg_id, args.cpu_seconds, args.format)
+        block["cpu_baseline"] = cpu_baseline(shape, cfg_id, args.cpu_seconds, args.format)
+    return block
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_quantized_moe_amd as moe
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py: no GPU")
+    moe.lib()  # fail loudly when the HIP library is missing
+    K, W = args.steps, args.warmup
+    first = args.workload if args.workload is not None else 2
+    main_block = measure(args, first, K, W)
+    if main_block is None:  # a profiling pass
+        return
+    line = {"metric": METRIC, "value": main_block.pop("value"), "unit": main_block.pop("unit"), "n_gpus": 1,
+            "steps": K, "warmup": W, "ms_per_step": main_block.pop("ms_per_step"), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": main_block.pop("dtype"), "data": "synthetic"}
+    line.update(main_block)
+    if args.workload is None:
+        line["decode_batch_32"] = measure(args, 3, K, W)
+        if not args.no_cpu_baseline:
+            line["cpu_oracle_1thread"] = cpu_oracle_1thread()
     print(json.dumps(line), flush=True)
 
 

@@ -2,11 +2,14 @@
 
 Integer outputs (sort, transpose) must match bit for bit; floating outputs
 must pass both the official and the strict rule of ``tests/parity.py``.
-Sizes: the small workloads are compared element by element; the largest
-decode workload (64 tokens, E=256, 5.5 GB of weights) is run at full size in
-the same launch configuration the benchmark uses and compared on sampled
-tokens, whose oracle values need only their own experts.
+Sizes: every workload is compared element by element at its full size; the
+largest decode workload (64 tokens, E=256, 5.5 GB of weights) runs in the
+same launch configuration the benchmark uses, its oracle spread over a
+thread pool one expert per task.
 """
+import concurrent.futures
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -126,42 +129,44 @@ def test_layer_prefill_kmajor_full():
     _full_check(Case(5), "cfg5")
 
 
-def test_layer_decode64_full_size_sampled():
-    """64 tokens, H=7168, I=2048, E=256, top-8: the full layer on the GPU,
-    the oracle on three sampled tokens (their h, y rows and output row)."""
-    say("layer cfg 4 full size, sampled tokens")
+def test_layer_decode64_full_size():
+    """64 tokens, H=7168, I=2048, E=256, top-8: the full layer on the GPU in
+    the launch configuration the benchmark uses (about 220 active experts,
+    5.5 GB of weights: persistent gate+up, nontemporal weight loads for the
+    experts read by one pass) against the oracle on every routed pair's h and
+    y row and every token's output row.  The oracle's per-expert work (its
+    own dequantisation, gate+up and down functions, as in moe_layer) runs on
+    a thread pool, one independent expert per task."""
+    say("layer cfg 4 full size, whole layer")
     case = Case(4)
     s = case.shape
     case.run()
     ref_sort = oracle.sort_routes(case.ids, s.E)
     _check_sort(case, ref_sort)
-    h = case.layer.h
-    y = case.layer.y
-    out = _h2f(case.layer.out)
-    wf = case.weight_fn()
     x = oracle.bf16_bits_to_f64(case.x_bits)
-    cache = {}
-    for t in (0, 31, 63):
-        o_ref = np.zeros(s.H)
-        hs, ys, hr, yr = [], [], [], []
-        for j in range(s.k):
-            e = int(case.ids[t, j])
-            if e not in cache:
-                cache.clear()
-                cache[e] = oracle.expert_weights(wf, e, s.H, s.I, False)
-            Wg, Wu, Wd = cache[e]
-            hh = oracle.gate_up_silu_rows(x[t][None], Wg, Wu)
-            yy = oracle.down_rows(hh, Wd)
-            p = int(ref_sort["pair_pos"][t * s.k + j])
-            hs.append(_h2f(h[p]))
-            ys.append(_h2f(y[p]))
-            hr.append(hh[0])
-            yr.append(yy[0])
-            o_ref += float(case.w[t, j]) * yy[0]
-        parity.assert_parity(np.array(hs), np.array(hr), f"cfg4 t{t} h")
-        parity.assert_parity(np.array(ys), np.array(yr), f"cfg4 t{t} y")
-        e = parity.assert_parity(out[t], o_ref, f"cfg4 t{t} out")
-        say("cfg4 token", t, e)
+    wf = case.weight_fn()
+    offs, tok = ref_sort["expert_offsets"], ref_sort["sorted_token_ids"]
+    active = [int(e) for e in ref_sort["active_experts"][: ref_sort["active_count"]]]
+    h_ref, y_ref = np.zeros((s.P, s.I)), np.zeros((s.P, s.H))
+
+    def one(e):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        Wg, Wu, Wd = oracle.expert_weights(wf, e, s.H, s.I, False)
+        hh = oracle.gate_up_silu_rows(x[tok[lo:hi]], Wg, Wu)
+        return lo, hi, hh, oracle.down_rows(hh, Wd)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for lo, hi, hh, yy in ex.map(one, active):
+            h_ref[lo:hi], y_ref[lo:hi] = hh, yy
+    out_ref = oracle.blend(y_ref, case.w, ref_sort["pair_pos"])
+    rows = np.diff(offs)
+    say("cfg4: active experts", len(active), "rows per expert max", int(rows.max()),
+        "experts with one row", int((rows == 1).sum()))
+    eh = parity.assert_parity(_h2f(case.layer.h), h_ref, "cfg4 h")
+    ey = parity.assert_parity(_h2f(case.layer.y), y_ref, "cfg4 y")
+    eo = parity.assert_parity(_h2f(case.layer.out), out_ref, "cfg4 out")
+    say("cfg4 h", eh, "y", ey, "out", eo)
 
 
 # ---------------------------------------------------------------- per-kernel, oracle inputs
