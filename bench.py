@@ -81,6 +81,9 @@ def parse():
                     help="gate and up as two K-major twins, or one concatenated twin (K-major workloads only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--measure", choices=["stream", "transpose"], default=None,
+                    help="instead of the step: the streaming-read ceiling over a 4 GiB buffer "
+                         "(moe_nvfp4_stream_read), or transpose_u8 over the many-token workload's weights")
     ap.add_argument("--profile-pass", choices=["gate_up", "down", "copy"], default=None,
                     help="for counter runs under rocprofv3: launch only gate+up+SiLU (after one sort), or "
                          "only the down projection (after one sort and gate+up), --steps times, or a plain "
@@ -494,6 +497,65 @@ def measure(args, cfg_id, K, W):
     return block
 
 
+def measure_aux(args):
+    """--measure: the streaming-read ceiling, or the load-time transpose's
+    throughput on the many-token workload's 192 weights (64 experts x gate,
+    up, down: packed and scale tensors), as GB/s of bytes read + written."""
+    import torch
+
+    import nvfp4_quantized_moe_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.measure == "stream":
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        buf.fill_(7)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        reps = 20
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                moe.moe_nvfp4_stream_read(buf, sink, stream)
+            e0.record(stream)
+            for _ in range(reps):
+                moe.moe_nvfp4_stream_read(buf, sink, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"measure": "stream_read", "bytes_per_launch": nbytes, "launch_us": round(ms * 1e3, 2),
+                "GBps": round(nbytes / (ms / 1e3) / 1e9, 1), "pct_of_8TBps": round(nbytes / (ms / 1e3) / 8e12 * 100, 1),
+                "launches": reps}
+    cfg = 5
+    shape = synth.config(cfg)
+    jobs = []
+    for e in range(shape.E):
+        for p in (0, 1, 2):
+            n, k = synth.proj_dims(shape, p)
+            pk, sc = synth.gen_expert(cfg, e, p, shape)
+            for src, rows, cols in ((pk, n, k // 2), (sc, n, k // 16)):
+                s_d = torch.from_numpy(src).to(dev)
+                jobs.append((s_d, torch.empty((cols, rows), dtype=torch.uint8, device=dev), rows, cols))
+    moved = 2 * sum(r * c for _, _, r, c in jobs)
+    reps = 5
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for s_d, d_d, r, c in jobs:
+            moe.transpose_u8(s_d, d_d, r, c, stream)
+        e0.record(stream)
+        for _ in range(reps):
+            for s_d, d_d, r, c in jobs:
+                moe.transpose_u8(s_d, d_d, r, c, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"measure": "transpose_u8", "workload": shape.name, "launches_per_pass": len(jobs),
+            "bytes_read_plus_written_per_pass": moved, "pass_us": round(ms * 1e3, 1),
+            "GBps": round(moved / (ms / 1e3) / 1e9, 1), "pct_of_8TBps": round(moved / (ms / 1e3) / 8e12 * 100, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -507,6 +569,9 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py: no GPU")
     moe.lib()  # fail loudly when the HIP library is missing
+    if args.measure:
+        print(json.dumps(measure_aux(args)), flush=True)
+        return
     K, W = args.steps, args.warmup
     first = args.workload if args.workload is not None else 2
     main_block = measure(args, first, K, W)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 6
+#define MOE_NVFP4_ABI_VERSION 7
 
 /* Weight layouts of a projection [N, K] (N outputs, K inputs). */
 #define MOE_NVFP4_ROW_MAJOR     0 /* packed [N, K/2], E4M3 scales [N, K/16]  (decode GEMV path)     */
@@ -346,6 +346,19 @@ int moe_nvfp4_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_
 
 /* ABI version of the loaded library (MOE_NVFP4_ABI_VERSION). */
 int moe_nvfp4_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Measurement support (not a step of the path).
+ * ------------------------------------------------------------------------
+ * moe_nvfp4_stream_read: read `bytes` of device memory at `src` once, in
+ * contiguous 1 KiB wave loads (8 per lane in flight), and discard the data:
+ * the streaming-read ceiling of this part, against which the decode path's
+ * weight bandwidth is read (a kernel that only streams reads, no arithmetic).
+ * `sink` is a device u32 that is written only in a case that does not occur
+ * for ordinary data (it keeps the loads from being removed).
+ * Errors: ENULL; ESHAPE if bytes < 16 or bytes % 16 != 0.
+ */
+int moe_nvfp4_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,7 @@ __all__ = [
     "moe_nvfp4_sort_gate_up_silu",
     "moe_nvfp4_sort_gate_up_launches",
     "moe_nvfp4_route",
+    "moe_nvfp4_stream_read",
     "with_shared_expert",
 ]
 
@@ -103,10 +104,11 @@ def lib() -> ctypes.CDLL:
                                                   _P, _P, _P, _P]
         L.moe_nvfp4_sort_gate_up_launches.argtypes = [_I, _I, _I, _I, _I, _I]
         L.moe_nvfp4_down_blend.argtypes = [_P, _I, _I, _I, _I, _I, _Experts, _P, _P, _P, _P, _P]
+        L.moe_nvfp4_stream_read.argtypes = [_P, ctypes.c_int64, _P, _P]
         for fn in ("moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                    "transpose_u8", "moe_nvfp4_route", "moe_nvfp4_abi_version", "transpose_u8_pitched",
                    "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
-                   "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend"):
+                   "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend", "moe_nvfp4_stream_read"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -374,6 +376,16 @@ def transpose_u8_pitched(src, dst, rows, cols, dst_pitch, dst_offset=0, stream=N
     rc = lib().transpose_u8_pitched(_dev(src, torch.uint8, "src"), _dev(dst, torch.uint8, "dst") + dst_offset,
                                     rows, cols, dst_pitch, _stream(stream))
     _check("transpose_u8_pitched", rc)
+
+
+def moe_nvfp4_stream_read(src, sink, stream=None) -> None:
+    """Read all of ``src`` (a contiguous device tensor) once and discard it:
+    the streaming-read ceiling (measurement support; see the C header)."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("moe_nvfp4_stream_read: src must be a contiguous device tensor")
+    rc = lib().moe_nvfp4_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                     _dev(sink, torch.int32, "sink", 1), _stream(stream))
+    _check("moe_nvfp4_stream_read", rc)
 
 
 def moe_nvfp4_route(logits, k, topk_ids, topk_weights, stream=None) -> None:

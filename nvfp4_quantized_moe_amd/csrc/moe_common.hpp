@@ -49,6 +49,7 @@ __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c) {
 // (HIP's uint4/float4 are structs whose copies go through a generic memcpy,
 // so 16-byte values move as a native 4 x u32 vector.)
 #define MOE_GLOBAL __attribute__((address_space(1)))
+#define MOE_LDS __attribute__((address_space(3)))
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 template <typename T>
@@ -150,6 +151,22 @@ __device__ __forceinline__ unsigned long long match_lanes(int e, bool valid, int
         eq &= bit ? m : ~m;
     }
     return eq;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; the LDS/scalar and
+// export counters left at their maxima, i.e. not waited for).  Loads count
+// down in issue order, so this waits for every load but the newest n.
+constexpr int waitcnt_vm(int n) { return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15); }
+
+// Workgroup barrier that waits for this wave's LDS operations only.  Direct
+// global-to-LDS loads count as vector-memory operations: a wave waits for its
+// own (waitcnt_vm) before the barrier that publishes them.  The asm fences
+// keep memory operations on their side.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float silu_f32(float z) {

@@ -57,6 +57,7 @@
 //     of bank conflicts.
 #include "moe_common.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace {
@@ -71,8 +72,10 @@ constexpr int kLdsBudget = 72 * 1024;  // staged activation rows per block (two 
 constexpr int kScaleLds = 1024;        // per wave: 4 steps x 8 rows x 32 bytes
 constexpr int kPreLds = 4 * (MOE_NVFP4_MAX_EXPERTS + 4);  // per-slot prefix sums of passes (or the fused sort)
 constexpr int kRmaxOff = kWaves * kScaleLds;                    // per-row maxima (16 x u32)
-constexpr int kPreOff = kRmaxOff + 64;
+constexpr int kTokOff = kRmaxOff + 64;                          // tokens of the pass's rows (16 x i32)
+constexpr int kPreOff = kTokOff + 64;
 constexpr int kHdrLds = kPreOff + kPreLds;  // scale areas + row maxima + pass prefix; then the rows
+constexpr int kRingFillLoads = 2 * kDepth + kDepth / kGroup;  // vector-memory loads that fill the ring
 
 using moe::u32x2_t;
 using moe::u32x4_t;
@@ -101,6 +104,7 @@ struct DecArgs {
     int extra;                  // block rows for passes beyond each expert's first
     int single_token;           // gate+up with T == 1: every routed row is token 0
     int nt_min_active;          // nontemporal weight loads from this many active experts on
+    int cap;                    // active-slot capacity, min(E, P)
     // Routing sort fused into the gate+up launch (few pairs, one pass per
     // expert): the routed ids, and the sort outputs that block (0, 0) writes.
     int fused_sort;
@@ -220,47 +224,55 @@ __device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v)
 // Stage rows [row0, row0 + pr) of the activation into LDS as fp16 (stride
 // ldx), row m scaled by 2^-e(m) where e(m) comes from the row's largest
 // magnitude (kept in rmax[m] as float bits; rmax is zero on entry).  Gate+up
-// gathers x rows by token (lane m < 16 of each wave holds row m's token in
-// tokv); down reads h rows in order, or (GATHER) row gpos[m] for row m.
-// mid() is called once the first loads are in flight and before any is
-// consumed, so the caller can queue more loads behind them.  Ends with the
-// rows visible to the whole block.
+// gathers x rows by token (row m's token in ptok[m], LDS); down reads h rows
+// in order, or (GATHER) row gpos[m] for row m.
+// mid() issues the weight ring: gate+up after every x load (mid() must issue
+// exactly kRingFillLoads loads), down once the first h loads are in flight.
+// Ends with the rows visible to the whole block.
 template <bool GATED, bool GATHER = false, typename Mid>
-__device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int tokv, uint16_t *xs, uint32_t *rmax,
-                                      Mid &&mid, const int *gpos = nullptr) {
+__device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const int *ptok, uint16_t *xs,
+                                      uint32_t *rmax, Mid &&mid, const int *gpos = nullptr) {
     const int K = a.K, ldx = a.ldx;
     auto hrow = [&](int m) -> size_t { return GATHER ? (size_t)gpos[m] : (size_t)(row0 + m); };
     const int cpr = K >> 3;  // 8-element chunks per row
     const int nch = pr * cpr;
-    constexpr int SB = GATED ? 8 : 4;  // chunks per thread per batch
+    constexpr int SB = 4;  // h: chunks per thread per batch
     // Unconditional LDS writes throughout: a chunk past the end re-writes
     // chunk 0 with its own value, and no load is left in flight on any path.
     if constexpr (GATED) {
-        auto batch = [&](int base, auto first) {
-            int ic[SB];
-            u32x4_t raw[SB];
-#pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int idx = base + i * kThreads + (int)threadIdx.x;
-                ic[i] = idx < nch ? idx : 0;
-                const int m = ic[i] / cpr, kc = ic[i] - m * cpr;
-                const int tok = __builtin_amdgcn_ds_bpermute(4 * m, tokv);
-                raw[i] = moe::gload<u32x4_t>(static_cast<const uint16_t *>(a.act) + (size_t)tok * K + 8 * kc);
-            }
-            if constexpr (decltype(first)::value) mid();
-#pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int m = ic[i] / cpr, kc = ic[i] - m * cpr;
-                const uint4 v = uint4{raw[i][0], raw[i][1], raw[i][2], raw[i][3]};
-                *reinterpret_cast<uint4 *>(xs + m * ldx + 8 * kc) = v;
-                if (base + i * kThreads < nch)  // uniform: the sub-batch holds real chunks
-                    row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
-            }
-        };
-        // The first batch is peeled so that mid() sits on a single path.
-        batch(0, std::true_type{});
-        for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
-        __syncthreads();  // bf16 rows and their maxima are complete
+        // x rows (bf16 bytes) straight into their LDS slots by direct loads,
+        // issued ahead of the weight ring (mid()): loads complete in issue
+        // order, so waiting for x then waits for no weight load.  One 16-byte
+        // slot per lane, 64 consecutive slots of the padded rows per
+        // instruction; a pad slot loads its row's first chunk (never read).
+        const uint16_t *x = static_cast<const uint16_t *>(a.act);
+        const int spr = ldx >> 3;  // 16-byte slots per staged row (chunks and pad)
+        const int nslot = pr * spr;
+        const int lane = threadIdx.x & 63, w = moe::wave_id();
+        uint8_t *xb = reinterpret_cast<uint8_t *>(xs);
+        for (int base = 64 * w; base < nslot; base += 64 * kWaves) {
+            const int sl = base + lane;
+            const int m = sl / spr, kc = sl - m * spr;
+            const int tok = ptok[m < pr ? m : 0];
+            if (sl < nslot)
+                __builtin_amdgcn_global_load_lds(
+                    (const MOE_GLOBAL void *)(x + (size_t)tok * K + 8 * (kc < cpr ? kc : 0)),
+                    (MOE_LDS void *)(xb + 16 * base), 16, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mid();
+        __builtin_amdgcn_s_waitcnt(moe::waitcnt_vm(kRingFillLoads));  // this wave's x slots have landed
+        moe::lds_barrier();
+        // Row maxima (lanes of a wave hold consecutive chunks; past the end,
+        // chunk 0 again).
+        for (int base = 0; base < nch; base += kThreads) {
+            const int idx = base + (int)threadIdx.x;
+            const int ic = idx < nch ? idx : 0;
+            const int m = ic / cpr, kc = ic - m * cpr;
+            const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * ldx + 8 * kc);
+            row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
+        }
+        moe::lds_barrier();  // maxima complete
         for (int idx = threadIdx.x; idx < nch; idx += kThreads) {  // bf16 -> scaled fp16 in place
             const int m = idx / cpr, kc = idx - m * cpr;
             const float f = exp2i(-row_exp(rmax[m]));
@@ -275,7 +287,7 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, int to
             }
             *reinterpret_cast<f16x8_t *>(p) = h;
         }
-        __syncthreads();
+        moe::lds_barrier();
     } else {
         const float *h = static_cast<const float *>(a.act);
         auto chunk = [&](int idx, int &m, int &kc) {
@@ -424,44 +436,36 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
         }
     };
 
-    if (threadIdx.x < 16) rmax[threadIdx.x] = 0u;
-    // Activation rows whose addresses need no lookup (down: h by position;
-    // gate+up with one token: x row 0) are loaded before the ring, so waiting
-    // for them waits for no weight.  Otherwise the lookup of the pass's tokens
-    // goes first, then ring slot 0, then the x rows, then the rest of the
-    // ring: the x rows wait for slot 0 only, and while they are converted the
-    // rest of the ring is in flight.
-    const bool x_first = !GATED || a.single_token;
-    int tokv = 0;  // gate+up: token of row (lane & 15) of the pass
-    if (!x_first) {
-        if constexpr (TOK_LDS)
-            tokv = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[row0 + min(lane & 15, pr - 1)];
-        else
-            tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    // The pass's row maxima are cleared and its tokens published in LDS
+    // (read there, no load result is pending when the activation loads go
+    // out).
+    // The activation rows are loaded before the ring (gate+up after the
+    // lookup of the pass's tokens, except with one token, whose row is x row
+    // 0), so waiting for them waits for no weight; the ring then fills while
+    // they are converted.
+    int *ptok = reinterpret_cast<int *>(lds + kTokOff);
+    if (threadIdx.x < 16) {
+        rmax[threadIdx.x] = 0u;
+        int tk = 0;  // one token: x row 0
+        if (GATED && !a.single_token) {
+            const int r = row0 + min((int)threadIdx.x, pr - 1);
+            if constexpr (TOK_LDS)
+                tk = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[r];
+            else
+                tk = moe::gload<int32_t>(a.sorted_tok + r);
+        }
+        ptok[threadIdx.x] = tk;
     }
-    __syncthreads();  // rmax cleared
+    __syncthreads();  // rmax cleared, tokens published
     __builtin_amdgcn_sched_barrier(0);
-    if (x_first) {
-        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                load(d);
-                __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-            }
-        });
-    } else {
-        load(0);
+    stage<GATED>(a, row0, pr, ptok, xs, rmax, [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int d = 1; d < D; ++d) {
-                load(d);
-                __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-            }
-        });
-    }
+        for (int d = 0; d < D; ++d) {
+            load(d);
+            __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+        }
+    });
 
     // One token group (pr <= 4): lane (n, q) feeds A row (token n >> 2,
     // quarter n & 3) and its output row is token q.
@@ -638,38 +642,29 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
         }
     };
 
-    if (threadIdx.x < 16) rmax[threadIdx.x] = 0u;
-    const bool x_first = !GATED || a.single_token;
-    int tokv = 0;
-    if (!x_first) {
-        if constexpr (TOK_LDS)
-            tokv = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[row0 + min(lane & 15, pr - 1)];
-        else
-            tokv = moe::gload<int32_t>(a.sorted_tok + row0 + min(lane & 15, pr - 1));
+    int *ptok = reinterpret_cast<int *>(lds + kTokOff);
+    if (threadIdx.x < 16) {
+        rmax[threadIdx.x] = 0u;
+        int tk = 0;  // one token: x row 0
+        if (GATED && !a.single_token) {
+            const int r = row0 + min((int)threadIdx.x, pr - 1);
+            if constexpr (TOK_LDS)
+                tk = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[r];
+            else
+                tk = moe::gload<int32_t>(a.sorted_tok + r);
+        }
+        ptok[threadIdx.x] = tk;
     }
-    __syncthreads();  // rmax cleared
+    __syncthreads();  // rmax cleared, tokens published
     __builtin_amdgcn_sched_barrier(0);
-    if (x_first) {
-        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                load(d);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        });
-    } else {
-        load(0);
+    stage<GATED>(a, row0, pr, ptok, xs, rmax, [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        stage<GATED>(a, row0, pr, tokv, xs, rmax, [&]() {
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int d = 1; d < D; ++d) {
-                load(d);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        });
-    }
+        for (int d = 0; d < D; ++d) {
+            load(d);
+            __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
+        }
+    });
 
     // A operand: row n of the pass (rows past it read row 0: dropped outputs).
     const int arow = (n < pr ? n : 0) * ldx;
@@ -950,32 +945,49 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
 
 // Relative cost of one unit of a pass with r routed rows (token groups of 4
 // share each decoded weight; the weight stream itself costs the same).
+// (A flatter model fitted to per-block timestamps, 12 + ceil(r / 4),
+// measured 2-3% slower on the 32- and 64-token launches.)
+constexpr int kUnitCostMax = 7;  // unit_cost(16)
+constexpr int kOnePassShares = 4;  // one pass per block when every pass is worth this many shares
 __device__ __forceinline__ int unit_cost(int r) { return 3 + ((r + 3) >> 2); }
 
-// Rows of active slot s.
-__device__ __forceinline__ int slot_rows(const DecArgs &a, int s) {
-    const int e = a.active[s];
-    return a.offsets[e + 1] - a.offsets[e];
-}
+// An active slot's expert, first sorted position and routed rows, cached in
+// LDS while a persistent block finds its share.
+struct SlotInfo {
+    int e, lo, rows;
+};
 
-// Block-wide exclusive prefix sum over the active slots of the cost of all
-// their passes (units x unit_cost per pass): pre[s] for s < n, pre[n] = total.
-__device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre) {
-    __shared__ int wsum[kWaves];
+// Block-wide: every slot's expert and row range (the active list is read
+// without waiting for the active count: its entries past the count are -1,
+// i.e. no rows), cached in si[s] for s < cap; and the exclusive prefix sum
+// over the active slots of the cost of all their passes (units x unit_cost
+// per pass): pre[s] for s < n, pre[n] = total.  Returns n.
+__device__ __forceinline__ int cost_prefix(const DecArgs &a, int *pre, SlotInfo *si, int &pass_min) {
+    __shared__ int wsum[kWaves], wmin[kWaves];
     const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
-    const int pr = a.pass_rows;
-    int c[4], sum = 0;
+    const int pr = a.pass_rows, cap = a.cap;
+    int e4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * t + i;
-        int cost = 0;
-        if (sl < n) {
-            const int r = slot_rows(a, sl);
-            const int full = r / pr, rem = r - full * pr;
-            cost = a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0));
+        e4[i] = sl < cap ? a.active[sl] : -1;
+    }
+    const int n = *a.nactive;  // read alongside the list
+    int c[4], sum = 0, cmin = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sl = 4 * t + i;
+        int lo = 0, r = 0;
+        if (e4[i] >= 0) {
+            lo = a.offsets[e4[i]];
+            r = a.offsets[e4[i] + 1] - lo;
         }
+        if (sl < cap) si[sl] = SlotInfo{e4[i], lo, r};
+        const int full = r / pr, rem = r - full * pr;
+        const int cost = sl < n ? a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0)) : 0;
         c[i] = cost;
         sum += cost;
+        if (sl < n) cmin = min(cmin, a.units * unit_cost(rem > 0 ? rem : pr));  // the slot's cheapest pass
     }
     int incl = sum;
 #pragma unroll
@@ -983,7 +995,9 @@ __device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre) {
         const int v = __shfl_up(incl, off, 64);
         if (lane >= off) incl += v;
     }
+    const uint32_t wm = moe::wave_min_u32((uint32_t)cmin);
     if (lane == 63) wsum[w] = incl;
+    if (lane == 0) wmin[w] = (int)wm;
     __syncthreads();
     int base = 0;
     for (int i = 0; i < w; ++i) base += wsum[i];
@@ -995,7 +1009,9 @@ __device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre) {
         run += c[i];
     }
     if (t == kThreads - 1) pre[n] = run;
+    pass_min = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
     __syncthreads();
+    return n;
 }
 
 // The first unit, in (slot, pass, unit) order, whose cost-weighted start is
@@ -1003,20 +1019,20 @@ __device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre) {
 struct Cursor {
     int s, p, u;
 };
-__device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, int n, int c) {
+__device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, const SlotInfo *si, int n, int c) {
     Cursor k{n, 0, 0};
     if (c >= pre[n]) return k;
     int s = find_slot(pre, n, c);
     int rem = c - pre[s];
     const int pr = a.pass_rows;
-    int r = slot_rows(a, s);
+    int r = si[s].rows;
     int p = 0;
     for (;;) {
         if (p * pr >= r) {  // past the slot's last pass: first unit of the next slot
             ++s;
             p = 0;
             if (s >= n) break;
-            r = slot_rows(a, s);
+            r = si[s].rows;
             rem = 0;
             continue;
         }
@@ -1042,34 +1058,83 @@ __device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, int n
 // (slot, pass, unit) in order, each unit weighted by unit_cost of its pass;
 // block b takes the units whose weighted start lies in the b-th equal share,
 // and streams them pass by pass.  Every block is busy for about the same
-// time and no block is launched only to find no work.
+// time and no block is launched only to find no work.  Set-up reads the
+// routing tables once: the slots' experts and row ranges are cached in LDS
+// (in the area the activation rows use later) and the share's first 64
+// slots move to registers (lane i: slot first + i) before the first pass
+// stages over them.
 template <bool GATED>
 __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     extern __shared__ uint4 lds4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
     int *pre = reinterpret_cast<int *>(lds + kPreOff);
-    const int n = *a.nactive;
-    cost_prefix(a, n, pre);
+    SlotInfo *si = reinterpret_cast<SlotInfo *>(lds + kHdrLds);
+    const int lane = threadIdx.x & 63;
+    int pass_min;
+    const int n = cost_prefix(a, pre, si, pass_min);
     const int total = pre[n];
     // Blocks go to the 8 XCDs round-robin; consecutive shares go to one XCD,
     // so the later passes of an expert mostly run where its earlier passes
     // left the weights in L2.
     const int g = gridDim.x;
     const int bx = (g & 7) == 0 ? (int)((blockIdx.x & 7) * (g >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
+    const bool nt_ok = a.nt_min_active > 0 && n >= a.nt_min_active;
+    if (n > 0 && (int64_t)pass_min * g >= (int64_t)kOnePassShares * total) {
+        // Every pass is worth several blocks' shares: block bx takes the pass
+        // whose cost range holds its point (bx + 1/2) total / g, and an even
+        // part of that pass's units among the blocks whose points fall in
+        // it.  Each block then stages once and streams one pass.  (With
+        // fewer shares per pass the whole-block rounding unbalances more
+        // than a second pass costs: the 64-token launch, about two shares
+        // per pass, measured 8% slower this way.)
+        const int64_t pt = ((int64_t)(2 * bx + 1) * total) / (2 * (int64_t)g);
+        const int sl = find_slot(pre, n, (int)pt);
+        const SlotInfo in = si[sl];
+        const int pr = a.pass_rows;
+        int64_t ps = pre[sl];
+        int p = 0, pc = 0;
+        for (;; ++p) {
+            pc = a.units * unit_cost(min(pr, in.rows - p * pr));
+            if (pt < ps + pc || (p + 1) * pr >= in.rows) break;
+            ps += pc;
+        }
+        // blocks whose points lie in [ps, ps + pc): (2b + 1) total in [2 g ps, 2 g (ps + pc))
+        auto first_at = [&](int64_t c) -> int64_t {
+            const int64_t v = 2 * (int64_t)g * c - total;
+            return v <= 0 ? 0 : (v + 2 * (int64_t)total - 1) / (2 * (int64_t)total);
+        };
+        const int b_lo = (int)first_at(ps), nb = (int)(first_at(ps + pc) - b_lo);
+        const int i = bx - b_lo;
+        const int u0 = (int)((int64_t)i * a.units / nb), u1 = (int)((int64_t)(i + 1) * a.units / nb);
+        __syncthreads();  // the set-up's readers of LDS are done
+        if (u1 > u0) do_pass_rows<GATED, false, true>(a, in.e, in.lo, in.lo + in.rows, p, u0, u1 - u0, nt_ok, lds);
+        return;
+    }
     const int c0 = (int)((int64_t)total * bx / g);
     const int c1 = (int)((int64_t)total * (bx + 1) / g);
-    Cursor k = locate(a, pre, n, c0);
-    const Cursor end = locate(a, pre, n, c1);
-    bool first = true;
+    Cursor k = locate(a, pre, si, n, c0);
+    const Cursor end = locate(a, pre, si, n, c1);
+    const int s_first = k.s;
+    SlotInfo mine{-1, 0, 0};
+    if (s_first + lane < n) mine = si[s_first + lane];
     while (k.s < n && (k.s < end.s || (k.s == end.s && (k.p < end.p || (k.p == end.p && k.u < end.u))))) {
         const bool last_item = k.s == end.s && k.p == end.p;
         const int ub = last_item ? end.u : a.units;
-        if (!first) __syncthreads();  // the previous pass's readers of LDS are done
-        first = false;
-        do_pass<GATED, true>(a, k.s, k.p, k.u, ub - k.u, n, lds);
+        __syncthreads();  // the set-up's (or the previous pass's) readers of LDS are done
+        const int i = k.s - s_first;
+        int e, lo, rows;
+        if (i < 64) {
+            e = __builtin_amdgcn_readlane(mine.e, i);
+            lo = __builtin_amdgcn_readlane(mine.lo, i);
+            rows = __builtin_amdgcn_readlane(mine.rows, i);
+        } else {  // a share over more than 64 slots (many experts with few rows)
+            e = a.active[k.s];
+            lo = a.offsets[e];
+            rows = a.offsets[e + 1] - lo;
+        }
+        do_pass_rows<GATED, false, true>(a, e, lo, lo + rows, k.p, k.u, ub - k.u, nt_ok, lds);
         // next (slot, pass)
-        const int r = slot_rows(a, k.s);
-        if ((k.p + 1) * a.pass_rows < r) {
+        if ((k.p + 1) * a.pass_rows < rows) {
             k = Cursor{k.s, k.p + 1, 0};
         } else {
             k = Cursor{k.s + 1, 0, 0};
@@ -1220,7 +1285,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
         };
 
         stage<false, true>(
-            a, 0, nlive, 0, xs, bl->rmax,
+            a, 0, nlive, nullptr, xs, bl->rmax,
             [&]() {
                 __builtin_amdgcn_sched_barrier(0);
                 if (nu > 0) {
@@ -1382,7 +1447,7 @@ DecConfig decode_config(bool gated, int N, int K, int P, int E) {
     const int nblk = 2 * moe_host::cu_count();
     const int64_t max_passes = (int64_t)(P - 1) / pr + cap;
     c.persistent = gated && (int64_t)cap * ((c.units + G - 1) / G) > 2 * (int64_t)nblk &&
-                   max_passes * c.units * 7 < ((int64_t)1 << 31);
+                   max_passes * c.units * kUnitCostMax < ((int64_t)1 << 31);
     // Further passes number at most sum_e floor((R_e - 1) / pr) <= (P - 1) / pr;
     // the grid's y extent is kept within its limit by striding over them.
     int extra = (P - 1) / pr;
@@ -1436,14 +1501,17 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     const int G = c.G;
     const int nblk = 2 * moe_host::cu_count();
     const int cap = E < P ? E : P;
+    a.cap = cap;
     if (c.persistent) {
+        // The set-up caches a SlotInfo per slot where the activation rows go.
+        const size_t plds = std::max(lds, (size_t)kHdrLds + sizeof(SlotInfo) * (size_t)cap);
         if (fuse) {
             const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
                                            fuse->pair_pos, fuse->active, fuse->active_count, fuse->err_flag,
                                            stream);
             if (rc != MOE_NVFP4_OK) return rc;
         }
-        hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), plds, stream, a);
         return moe_host::launch_status();
     }
     const int extra = c.extra;

@@ -48,7 +48,6 @@ using moe::u32x4_t;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
-#define MOE_LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
 constexpr int kBK = 32;     // k per step
@@ -131,22 +130,11 @@ __device__ __forceinline__ void decode_b(const uint32_t (&w)[4], uint32_t s, bf1
     }
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory loads of this
-// wave are outstanding (vmcnt in bits 3:0 and 15:14; LDS/scalar and export
-// counters left at their maxima, i.e. not waited for).
-constexpr int waitcnt_vm(int n) { return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15); }
-
-// Workgroup barrier without the release fence of __syncthreads: that fence
-// would wait for every outstanding load (direct loads into LDS count as
-// outstanding stores), emptying the prefetch rings at every step.  Callers
-// wait for the direct loads the other waves need by count; this wave's LDS
-// writes are waited for here, and the asm fences keep memory operations on
-// their side.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+using moe::waitcnt_vm;
+// Workgroup barrier without the release fence of __syncthreads, so no
+// outstanding load is drained: callers wait for the direct loads the other
+// waves need by count (waitcnt_vm).
+__device__ __forceinline__ void block_barrier() { moe::lds_barrier(); }
 
 // Swizzle of the 16-byte octet of staged row r: conflict-free operand reads
 // whether the LDS serves 16 lanes x 16 bytes per cycle (64 banks) or 8 lanes

@@ -18,10 +18,10 @@ def test_library_exports_every_header_function():
     assert set(names) >= {"moe_nvfp4_sort", "moe_nvfp4_gate_up_silu", "moe_nvfp4_down", "moe_nvfp4_blend",
                           "transpose_u8", "moe_nvfp4_abi_version", "moe_nvfp4_route", "transpose_u8_pitched",
                           "moe_nvfp4_gate_up_silu_concat", "moe_nvfp4_sort_gate_up_silu",
-                          "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend"}
+                          "moe_nvfp4_sort_gate_up_launches", "moe_nvfp4_down_blend", "moe_nvfp4_stream_read"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_nvfp4_abi_version() == 6
+    assert L.moe_nvfp4_abi_version() == 7
 
 
 def _ex(layout=0, null=False):
@@ -82,6 +82,15 @@ def test_down_and_blend_and_transpose_reject():
     assert L.moe_nvfp4_blend(D, D, D, 4, 2, 1 << 17, D, None) == ELIMIT
     assert L.transpose_u8(None, D, 4, 4, None) == ENULL
     assert L.transpose_u8(D, D, 0, 4, None) == ESHAPE
+
+
+def test_stream_read_rejects():
+    L = moe.lib()
+    L.moe_nvfp4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.moe_nvfp4_stream_read(None, 1024, D, None) == ENULL
+    assert L.moe_nvfp4_stream_read(D, 1024, None, None) == ENULL
+    assert L.moe_nvfp4_stream_read(D, 8, D, None) == ESHAPE
+    assert L.moe_nvfp4_stream_read(D, 1000, D, None) == ESHAPE
 
 
 def test_python_binding_checks_tensor_arguments():
