@@ -180,6 +180,122 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// ---------------------------------------------------------------------------
+// Routing sort of P <= 256 pairs by one 256-thread block, in LDS: one pair per
+// thread; an LDS histogram of all pairs and one per wave; a pair's sorted
+// position is its expert's offset, plus the pairs of its id in earlier
+// waves, plus those in earlier lanes of its own wave (so positions follow the
+// flat pair index and the result is unique).  LDS (caller's): offs[E + 1]
+// (on return the exclusive offsets, offs[E] = valid pairs), cntw[4 * E],
+// act[E] (on return the active experts ascending), stok[P] (on return the
+// token of each sorted position below offs[E]).  Returns the active count.
+// With `out` set, also writes every output of moe_nvfp4_sort to memory.
+// Ends with a barrier.
+struct SortOutputs {
+    int32_t *offsets, *sorted_tok, *pair_pos, *active, *active_count;
+    uint32_t *err_flag;
+};
+constexpr int kBlockSortPairs = 256;
+__device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, int E, int *offs, int *cntw,
+                                              int *act, int *stok, const SortOutputs *out) {
+    __shared__ int wsum[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = tid < P ? ids[tid] : -1;
+    const bool valid = tid < P && e >= 0 && e < E;
+    for (int i = tid; i < E; i += 256) {
+        offs[i] = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cntw[w * E + i] = 0;
+    }
+    if (out && __ballot(tid < P && !valid) != 0ull && lane == 0)
+        atomicOr(out->err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
+    __syncthreads();
+    if (valid) {
+        atomicAdd(&offs[e], 1);
+        atomicAdd(&cntw[wave * E + e], 1);
+    }
+    __syncthreads();
+
+    // Exclusive scans over the experts (4 consecutive per thread) of the
+    // counts and of the active flags.
+    int c[4], s0 = 0, s1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ex = 4 * tid + i;
+        c[i] = ex < E ? offs[ex] : 0;
+        s0 += c[i];
+        s1 += c[i] > 0 ? 1 : 0;
+    }
+    int i0 = s0, i1 = s1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o0 = __shfl_up(i0, d, 64), o1 = __shfl_up(i1, d, 64);
+        if (lane >= d) {
+            i0 += o0;
+            i1 += o1;
+        }
+    }
+    if (lane == 63) {
+        wsum[0][wave] = i0;
+        wsum[1][wave] = i1;
+    }
+    __syncthreads();
+    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) {
+            b0 += wsum[0][w];
+            b1 += wsum[1][w];
+        }
+        t0 += wsum[0][w];
+        t1 += wsum[1][w];
+    }
+    int off = b0 + i0 - s0, aidx = b1 + i1 - s1;
+    __syncthreads();  // every count is read before the offsets replace them
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ex = 4 * tid + i;
+        if (ex < E) {
+            offs[ex] = off;
+            if (c[i] > 0) act[aidx] = ex;
+            if (out) {
+                out->offsets[ex] = off;
+                if (c[i] > 0) out->active[aidx] = ex;
+                if (ex >= t1) out->active[ex] = -1;
+            }
+            aidx += c[i] > 0 ? 1 : 0;
+        }
+        off += c[i];
+    }
+    if (tid == 0) {
+        offs[E] = t0;
+        if (out) {
+            out->offsets[E] = t0;
+            *out->active_count = t1;
+        }
+    }
+    __syncthreads();
+
+    if (wave * 64 < P) {
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        int rank = __popcll(match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
+        if (valid)
+            for (int w = 0; w < wave; ++w) rank += cntw[w * E + e];
+        if (tid < P) {
+            const int pos = valid ? offs[e] + rank : -1;
+            if (valid) stok[pos] = tid / k;
+            if (out) {
+                out->pair_pos[tid] = pos;
+                if (valid) out->sorted_tok[pos] = tid / k;
+            }
+        }
+    }
+    if (out)
+        for (int q = t0 + tid; q < P; q += 256) out->sorted_tok[q] = -1;
+    __syncthreads();
+    return t1;
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------------------

@@ -367,10 +367,11 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
 // One pass: rows [row0, row0 + pr) of the expert against units
 // [u_first, u_first + nu) of its weights.
 // A pass of up to 4 rows in the (row, quarter) layout.
-template <bool GATED, int D, bool TOK_LDS, bool NT>  // TOK_LDS: pass tokens from the fused sort's LDS table
+template <bool GATED, int D, bool TOK_LDS, bool NT>  // TOK_LDS: tokens from the fused sort's LDS table tokl
 __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                          const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
-                                         const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
+                                         const uint8_t *sB, float s2A, float s2B, uint8_t *lds,
+                                         const int *tokl) {
     static_assert(D % kGroup == 0, "ring depth");
     const int K = a.K, N = a.N, ldx = a.ldx;
     const int rowbytes = K >> 1, sbytes = K >> 4;
@@ -450,7 +451,7 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
         if (GATED && !a.single_token) {
             const int r = row0 + min((int)threadIdx.x, pr - 1);
             if constexpr (TOK_LDS)
-                tk = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[r];
+                tk = tokl[r];
             else
                 tk = moe::gload<int32_t>(a.sorted_tok + r);
         }
@@ -578,7 +579,8 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
 template <bool GATED, int D, bool TOK_LDS>
 __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int pr, int u_first, int nu,
                                                const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
-                                               const uint8_t *sB, float s2A, float s2B, uint8_t *lds) {
+                                               const uint8_t *sB, float s2A, float s2B, uint8_t *lds,
+                                               const int *tokl) {
     static_assert(D % kGroup == 0, "ring depth");
     const int K = a.K, N = a.N, ldx = a.ldx;
     const int rowbytes = K >> 1, sbytes = K >> 4;
@@ -649,7 +651,7 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
         if (GATED && !a.single_token) {
             const int r = row0 + min((int)threadIdx.x, pr - 1);
             if constexpr (TOK_LDS)
-                tk = reinterpret_cast<const SortLds *>(lds + kPreOff)->tok[r];
+                tk = tokl[r];
             else
                 tk = moe::gload<int32_t>(a.sorted_tok + r);
         }
@@ -798,7 +800,7 @@ __device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
 // One pass of expert e, whose rows are the sorted positions [lo, hi).
 template <bool GATED, bool TOK_LDS, bool NT_OK>  // NT_OK: built with the nontemporal variant
 __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, int hi, int pass, int u_first,
-                                             int nu, bool nt_ok, uint8_t *lds) {
+                                             int nu, bool nt_ok, uint8_t *lds, const int *tokl = nullptr) {
     // Every table entry of expert e is read at once (e < E, so each read is
     // in bounds): one round of dependent loads, not one per table.
     const uint8_t *pA = a.pa[e];
@@ -827,11 +829,11 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
     // Nontemporal weight loads: a large launch, and an expert read by this
     // pass alone.
     if (pr > 4)
-        run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+        run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
     else if (NT_OK && nt_ok && rows <= a.pass_rows)
-        run_pass<GATED, kDepth, TOK_LDS, NT_OK>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+        run_pass<GATED, kDepth, TOK_LDS, NT_OK>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
     else
-        run_pass<GATED, kDepth, TOK_LDS, false>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds);
+        run_pass<GATED, kDepth, TOK_LDS, false>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
 }
 
 template <bool GATED, bool NT_OK>
@@ -923,7 +925,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     if constexpr (GATED && SORT) {  // extra == 0: one pass per expert
         const int3 r = fused_sort(a, reinterpret_cast<SortLds *>(lds + kPreOff), y);
         if (r.x < 0) return;  // past the active count
-        do_pass_rows<GATED, true, false>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, false, lds);
+        do_pass_rows<GATED, true, false>(a, r.x, r.y, r.y + r.z, 0, u_first, nu, false, lds,
+                                         reinterpret_cast<const SortLds *>(lds + kPreOff)->tok);
         return;
     }
     if (y >= a.extra) {
@@ -957,32 +960,24 @@ struct SlotInfo {
     int e, lo, rows;
 };
 
-// Block-wide: every slot's expert and row range (the active list is read
-// without waiting for the active count: its entries past the count are -1,
-// i.e. no rows), cached in si[s] for s < cap; and the exclusive prefix sum
-// over the active slots of the cost of all their passes (units x unit_cost
-// per pass): pre[s] for s < n, pre[n] = total.  Returns n.
-__device__ __forceinline__ int cost_prefix(const DecArgs &a, int *pre, SlotInfo *si, int &pass_min) {
+// Block-wide: every slot's expert and row range (slot(sl) for sl < cap,
+// an expert of -1 past the active count), cached in si[sl]; and the
+// exclusive prefix sum over the n active slots of the cost of all their
+// passes (units x unit_cost per pass): pre[s] for s < n, pre[n] = total.
+// pass_min: the cost of the cheapest pass.
+template <typename SlotFn>
+__device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre, SlotInfo *si, int &pass_min,
+                                            SlotFn &&slot) {
     __shared__ int wsum[kWaves], wmin[kWaves];
     const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
     const int pr = a.pass_rows, cap = a.cap;
-    int e4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int sl = 4 * t + i;
-        e4[i] = sl < cap ? a.active[sl] : -1;
-    }
-    const int n = *a.nactive;  // read alongside the list
     int c[4], sum = 0, cmin = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * t + i;
-        int lo = 0, r = 0;
-        if (e4[i] >= 0) {
-            lo = a.offsets[e4[i]];
-            r = a.offsets[e4[i] + 1] - lo;
-        }
-        if (sl < cap) si[sl] = SlotInfo{e4[i], lo, r};
+        const SlotInfo in = sl < cap ? slot(sl) : SlotInfo{-1, 0, 0};
+        const int r = in.rows;
+        if (sl < cap) si[sl] = in;
         const int full = r / pr, rem = r - full * pr;
         const int cost = sl < n ? a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0)) : 0;
         c[i] = cost;
@@ -1011,7 +1006,6 @@ __device__ __forceinline__ int cost_prefix(const DecArgs &a, int *pre, SlotInfo 
     if (t == kThreads - 1) pre[n] = run;
     pass_min = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
     __syncthreads();
-    return n;
 }
 
 // The first unit, in (slot, pass, unit) order, whose cost-weighted start is
@@ -1063,15 +1057,44 @@ __device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, const
 // (in the area the activation rows use later) and the share's first 64
 // slots move to registers (lane i: slot first + i) before the first pass
 // stages over them.
-template <bool GATED>
+template <bool GATED, bool SORT>  // SORT: the routing sort runs in every block (P <= 256; block 0 writes it)
 __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     extern __shared__ uint4 lds4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
     int *pre = reinterpret_cast<int *>(lds + kPreOff);
-    SlotInfo *si = reinterpret_cast<SlotInfo *>(lds + kHdrLds);
     const int lane = threadIdx.x & 63;
-    int pass_min;
-    const int n = cost_prefix(a, pre, si, pass_min);
+    int pass_min, n;
+    SlotInfo *si;
+    const int *tokl = nullptr;
+    if constexpr (SORT) {
+        // Set-up area (where the activation rows go later): offsets[E + 1],
+        // per-wave histograms [4 E], active list [E], sorted tokens [P],
+        // then the slot cache.
+        int *offs = reinterpret_cast<int *>(lds + kHdrLds);
+        int *cntw = offs + a.E + 1;
+        int *act = cntw + 4 * a.E;
+        int *stok = act + a.E;
+        si = reinterpret_cast<SlotInfo *>(stok + a.P);
+        const moe::SortOutputs out{a.sort_offsets, a.sort_tok, a.sort_pos, a.sort_active, a.sort_count, a.err_flag};
+        n = moe::block_sort_256(a.topk_ids, a.P, a.topk, a.E, offs, cntw, act, stok,
+                                blockIdx.x == 0 ? &out : nullptr);
+        tokl = stok;
+        cost_prefix(a, n, pre, si, pass_min, [&](int sl) {
+            const int e = sl < n ? act[sl] : -1;
+            return e < 0 ? SlotInfo{-1, 0, 0} : SlotInfo{e, offs[e], offs[e + 1] - offs[e]};
+        });
+    } else {
+        si = reinterpret_cast<SlotInfo *>(lds + kHdrLds);
+        // The active list is read without waiting for the active count:
+        // its entries past the count are -1.
+        n = *a.nactive;
+        cost_prefix(a, n, pre, si, pass_min, [&](int sl) {
+            const int e = a.active[sl];
+            if (e < 0) return SlotInfo{-1, 0, 0};
+            const int lo = a.offsets[e];
+            return SlotInfo{e, lo, a.offsets[e + 1] - lo};
+        });
+    }
     const int total = pre[n];
     // Blocks go to the 8 XCDs round-robin; consecutive shares go to one XCD,
     // so the later passes of an expert mostly run where its earlier passes
@@ -1107,32 +1130,46 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         const int i = bx - b_lo;
         const int u0 = (int)((int64_t)i * a.units / nb), u1 = (int)((int64_t)(i + 1) * a.units / nb);
         __syncthreads();  // the set-up's readers of LDS are done
-        if (u1 > u0) do_pass_rows<GATED, false, true>(a, in.e, in.lo, in.lo + in.rows, p, u0, u1 - u0, nt_ok, lds);
+        if (u1 > u0)
+            do_pass_rows<GATED, SORT, true>(a, in.e, in.lo, in.lo + in.rows, p, u0, u1 - u0, nt_ok, lds, tokl);
         return;
     }
     const int c0 = (int)((int64_t)total * bx / g);
     const int c1 = (int)((int64_t)total * (bx + 1) / g);
     Cursor k = locate(a, pre, si, n, c0);
     const Cursor end = locate(a, pre, si, n, c1);
+    // The share's first slots move to registers (lane l, entry j: slot
+    // s_first + l + 64 j), every slot of the launch when the sort runs here
+    // (P <= 256 pairs, so at most 256 slots).
     const int s_first = k.s;
-    SlotInfo mine{-1, 0, 0};
-    if (s_first + lane < n) mine = si[s_first + lane];
+    constexpr int kRegSlots = SORT ? 4 : 1;
+    SlotInfo mine[kRegSlots];
+#pragma unroll
+    for (int j = 0; j < kRegSlots; ++j) {
+        const int sl = s_first + lane + 64 * j;
+        mine[j] = sl < n ? si[sl] : SlotInfo{-1, 0, 0};
+    }
     while (k.s < n && (k.s < end.s || (k.s == end.s && (k.p < end.p || (k.p == end.p && k.u < end.u))))) {
         const bool last_item = k.s == end.s && k.p == end.p;
         const int ub = last_item ? end.u : a.units;
         __syncthreads();  // the set-up's (or the previous pass's) readers of LDS are done
         const int i = k.s - s_first;
-        int e, lo, rows;
-        if (i < 64) {
-            e = __builtin_amdgcn_readlane(mine.e, i);
-            lo = __builtin_amdgcn_readlane(mine.lo, i);
-            rows = __builtin_amdgcn_readlane(mine.rows, i);
-        } else {  // a share over more than 64 slots (many experts with few rows)
+        int e = -1, lo = 0, rows = 0;
+        if (i < 64 * kRegSlots) {
+#pragma unroll
+            for (int j = 0; j < kRegSlots; ++j) {
+                if (i >> 6 == j) {
+                    e = __builtin_amdgcn_readlane(mine[j].e, i & 63);
+                    lo = __builtin_amdgcn_readlane(mine[j].lo, i & 63);
+                    rows = __builtin_amdgcn_readlane(mine[j].rows, i & 63);
+                }
+            }
+        } else if constexpr (!SORT) {  // a share over more than 64 slots (many experts with few rows)
             e = a.active[k.s];
             lo = a.offsets[e];
             rows = a.offsets[e + 1] - lo;
         }
-        do_pass_rows<GATED, false, true>(a, e, lo, lo + rows, k.p, k.u, ub - k.u, nt_ok, lds);
+        do_pass_rows<GATED, SORT, true>(a, e, lo, lo + rows, k.p, k.u, ub - k.u, nt_ok, lds, tokl);
         // next (slot, pass)
         if ((k.p + 1) * a.pass_rows < rows) {
             k = Cursor{k.s, k.p + 1, 0};
@@ -1456,8 +1493,11 @@ DecConfig decode_config(bool gated, int N, int K, int P, int E) {
 }
 
 // The routing sort runs inside the gate+up launch when every expert's rows
-// fit one pass (no further-pass block rows) and the pairs fit a wave.
-bool decode_sort_fuses(const DecConfig &c, int P) { return !c.persistent && c.extra == 0 && P <= kSortPairs; }
+// fit one pass (no further-pass block rows) and the pairs fit a wave, or
+// when the launch is persistent and the pairs fit one block's sort.
+bool decode_sort_fuses(const DecConfig &c, int P) {
+    return c.persistent ? P <= moe::kBlockSortPairs : (c.extra == 0 && P <= kSortPairs);
+}
 
 }  // namespace
 
@@ -1503,15 +1543,33 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     const int cap = E < P ? E : P;
     a.cap = cap;
     if (c.persistent) {
-        // The set-up caches a SlotInfo per slot where the activation rows go.
-        const size_t plds = std::max(lds, (size_t)kHdrLds + sizeof(SlotInfo) * (size_t)cap);
-        if (fuse) {
+        // The set-up caches a SlotInfo per slot where the activation rows go
+        // (with the sort in the launch: after its LDS tables).
+        size_t setup = sizeof(SlotInfo) * (size_t)cap;
+        const bool sort_here = fuse && decode_sort_fuses(c, P);
+        if (sort_here) {
+            setup += sizeof(int) * (size_t)(6 * E + 1 + P);
+            a.P = P;
+            a.topk = fuse->k;
+            a.E = E;
+            a.topk_ids = fuse->topk_ids;
+            a.sort_offsets = fuse->offsets;
+            a.sort_tok = fuse->sorted_tok;
+            a.sort_pos = fuse->pair_pos;
+            a.sort_active = fuse->active;
+            a.sort_count = fuse->active_count;
+            a.err_flag = fuse->err_flag;
+        } else if (fuse) {
             const int rc = moe_launch_sort(fuse->topk_ids, T, fuse->k, E, fuse->offsets, fuse->sorted_tok,
                                            fuse->pair_pos, fuse->active, fuse->active_count, fuse->err_flag,
                                            stream);
             if (rc != MOE_NVFP4_OK) return rc;
         }
-        hipLaunchKernelGGL(k_decode_row_persist<true>, dim3(nblk), dim3(kThreads), plds, stream, a);
+        const size_t plds = std::max(lds, (size_t)kHdrLds + setup);
+        if (sort_here)
+            hipLaunchKernelGGL((k_decode_row_persist<true, true>), dim3(nblk), dim3(kThreads), plds, stream, a);
+        else
+            hipLaunchKernelGGL((k_decode_row_persist<true, false>), dim3(nblk), dim3(kThreads), plds, stream, a);
         return moe_host::launch_status();
     }
     const int extra = c.extra;

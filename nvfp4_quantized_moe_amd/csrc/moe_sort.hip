@@ -157,97 +157,19 @@ __global__ __launch_bounds__(kSortThreads) void k_moe_sort(
 // expert's offset, plus the pairs of its id in earlier waves, plus those in
 // earlier lanes of its own wave.  Same results as k_moe_sort.
 constexpr int kSmallThreads = 256;
-constexpr int kSmallPairs = kSmallThreads;
+constexpr int kSmallPairs = moe::kBlockSortPairs;
 constexpr int kSmallWaves = kSmallThreads / 64;
 
 __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     const int32_t *__restrict__ ids, int P, int k, int E, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_tok, int32_t *__restrict__ pair_pos, int32_t *__restrict__ active,
     int32_t *__restrict__ active_count, uint32_t *__restrict__ err_flag) {
-    __shared__ int cnt[MOE_NVFP4_MAX_EXPERTS];
-    __shared__ int cntw[kSmallWaves][MOE_NVFP4_MAX_EXPERTS];  // per-wave histograms
-    __shared__ int wsum[2][kSmallWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e = tid < P ? ids[tid] : -1;
-    const bool valid = tid < P && e >= 0 && e < E;
-    for (int i = tid; i < E; i += kSmallThreads) {
-        cnt[i] = 0;
-#pragma unroll
-        for (int w = 0; w < kSmallWaves; ++w) cntw[w][i] = 0;
-    }
-    if (__ballot(tid < P && !valid) != 0ull && lane == 0) atomicOr(err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
-    __syncthreads();
-    if (valid) {
-        atomicAdd(&cnt[e], 1);
-        atomicAdd(&cntw[wave][e], 1);
-    }
-    __syncthreads();
-
-    // Exclusive scans over the experts (4 consecutive per thread) of the
-    // counts and of the active flags.
-    int c[4], s0 = 0, s1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ex = 4 * tid + i;
-        c[i] = ex < E ? cnt[ex] : 0;
-        s0 += c[i];
-        s1 += c[i] > 0 ? 1 : 0;
-    }
-    int i0 = s0, i1 = s1;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o0 = __shfl_up(i0, d, 64), o1 = __shfl_up(i1, d, 64);
-        if (lane >= d) {
-            i0 += o0;
-            i1 += o1;
-        }
-    }
-    if (lane == 63) {
-        wsum[0][wave] = i0;
-        wsum[1][wave] = i1;
-    }
-    __syncthreads();
-    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-        if (w < wave) {
-            b0 += wsum[0][w];
-            b1 += wsum[1][w];
-        }
-        t0 += wsum[0][w];
-        t1 += wsum[1][w];
-    }
-    int off = b0 + i0 - s0, aidx = b1 + i1 - s1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ex = 4 * tid + i;
-        if (ex < E) {
-            offsets[ex] = off;
-            cnt[ex] = off;  // base of the expert's positions, read by the ranking below
-            if (c[i] > 0) active[aidx++] = ex;
-            if (ex >= t1) active[ex] = -1;
-        }
-        off += c[i];
-    }
-    if (tid == 0) {
-        offsets[E] = t0;
-        *active_count = t1;
-    }
-    __syncthreads();
-
-    if (wave * 64 < P) {
-        // Stable rank among equal ids: threads are in flat pair order.
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        int rank = __popcll(moe::match_lanes(e, valid, E > 1 ? 32 - __clz(E - 1) : 0) & lt);
-        if (valid)
-            for (int w = 0; w < wave; ++w) rank += cntw[w][e];
-        if (tid < P) {
-            const int pos = valid ? cnt[e] + rank : -1;
-            pair_pos[tid] = pos;
-            if (valid) sorted_tok[pos] = tid / k;
-        }
-    }
-    for (int p = t0 + tid; p < P; p += kSmallThreads) sorted_tok[p] = -1;
+    __shared__ int offs[MOE_NVFP4_MAX_EXPERTS + 1];
+    __shared__ int cntw[kSmallWaves * MOE_NVFP4_MAX_EXPERTS];  // per-wave histograms
+    __shared__ int act[MOE_NVFP4_MAX_EXPERTS];
+    __shared__ int stok[kSmallPairs];
+    const moe::SortOutputs out{offsets, sorted_tok, pair_pos, active, active_count, err_flag};
+    moe::block_sort_256(ids, P, k, E, offs, cntw, act, stok, &out);
 }
 
 }  // namespace

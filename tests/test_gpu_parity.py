@@ -498,12 +498,19 @@ def test_ragged_concat_gate_up(T, H, I, E, k, fmt):
 @pytest.mark.parametrize("T,k,E,H,I,mode", [(1, 8, 128, 2048, 768, "rand"), (4, 2, 4, 256, 512, "rand"),
                                              (2, 8, 1024, 256, 256, "invalid"), (3, 5, 7, 512, 256, "dup"),
                                              (16, 3, 4, 512, 256, "dup"), (2, 32, 64, 256, 384, "rand"),
-                                             (32, 6, 128, 2688, 1856, "rand")])
+                                             (32, 6, 128, 2688, 1856, "rand"), (40, 6, 128, 2688, 1856, "invalid"),
+                                             (42, 6, 100, 512, 2048, "dup"), (43, 6, 128, 512, 2048, "rand")])
 def test_sort_fused_into_gate_up_matches_two_calls(T, k, E, H, I, mode):
     """moe_nvfp4_sort_gate_up_silu (one launch while P <= 64 and each expert
-    fits one pass; two launches otherwise) against the two separate calls:
-    sort outputs and err_flag equal, h bit for bit; sort outputs against the
+    fits one pass, or when the gate+up launch is persistent and P <= 256:
+    every block then sorts in LDS and block 0 writes the sort outputs; two
+    launches otherwise, e.g. 258 pairs) against the two separate calls: sort
+    outputs and err_flag equal, h bit for bit; sort outputs against the
     oracle's brute force."""
+    L1 = moe.moe_nvfp4_sort_gate_up_launches(T, k, E, H, I, moe.ROW_MAJOR)
+    say("launches", L1)
+    if T * k in (192, 240, 252):
+        assert L1 == 1
     say("fused sort", T, k, E, H, I, mode)
     shape = synth.MoeShape(f"fs_{T}_{k}_{E}", T, H, I, E, k, "uniform", False)
     rng = np.random.default_rng(T * 1000 + E)
