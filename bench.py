@@ -19,9 +19,14 @@ workload alone.
 
 The K timed steps are captured into one HIP graph.  It is replayed once
 untimed (the first replay of a graph also uploads it), then a 1 GiB buffer
-is rewritten to evict the caches, then the timed replay runs between a
-device synchronisation on each side (``--eager`` launches the steps one by
-one instead).  A one-wave spin kernel of about a millisecond runs just ahead
+is read through once to evict the caches, the W warm-up steps (other weight
+copies than the timed ones) run once more, and the timed replay runs
+between a device synchronisation on each side (``--eager`` launches the
+steps one by one instead).  The eviction reads rather than writes: a
+rewritten buffer left the Infinity Cache full of dirty lines, whose write-
+back slowed the first dozen steps after it (a 20-step replay of the 1-token
+step measured 20.0 us per step against 17.1 us over 2000 steps; with the
+read and the warm-up replay, 18.0 us).  A one-wave spin kernel of about a millisecond runs just ahead
 of the start event, so that the host has submitted the replay before the
 timed region opens (otherwise a fixed submission latency of the order of
 50 us lands in it, a few percent of a 20-step replay).  Reported on one JSON line, per workload:
@@ -232,13 +237,18 @@ def cpu_oracle_1thread():
 
 
 def flush_caches(dev, scratch=[]):
-    """Rewrite a 1 GiB device buffer (more than the 256 MB Infinity Cache and
-    the L2s together), so the next step finds nothing of its weights cached."""
+    """Read a 1 GiB device buffer once with the library's streaming-read
+    kernel (more than the 256 MB Infinity Cache and the L2s together), so the
+    next step finds nothing of its weights cached and no dirty line to write
+    back."""
     import torch
 
+    import nvfp4_quantized_moe_amd as moe
+
     if not scratch:
-        scratch.append(torch.empty(1 << 30, dtype=torch.uint8, device=dev))
-    scratch[0].fill_(1)
+        scratch.append(torch.ones(1 << 30, dtype=torch.uint8, device=dev))
+        scratch.append(torch.zeros(1, dtype=torch.int32, device=dev))
+    moe.moe_nvfp4_stream_read(scratch[0], scratch[1])
 
 
 def measure(args, cfg_id, K, W):
@@ -380,9 +390,9 @@ def measure(args, cfg_id, K, W):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     if args.eager:
+        flush_caches(dev)
         with torch.cuda.stream(stream):
             run_steps(0, W, stream)
-        flush_caches(dev)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             torch.cuda._sleep(SPIN_CYCLES)
@@ -393,7 +403,8 @@ def measure(args, cfg_id, K, W):
     else:
         # Warm-up steps run as their own graph; the timed graph is replayed
         # once untimed (its first replay uploads it), the caches are flushed,
-        # and its next replay is timed.
+        # the warm-up graph runs again, and the timed graph's next replay is
+        # timed.
         g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_warm, stream=stream):
             run_steps(0, max(W, 1), stream)
@@ -404,6 +415,7 @@ def measure(args, cfg_id, K, W):
         g_main.replay()
         torch.cuda.synchronize()
         flush_caches(dev)
+        g_warm.replay()
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             # The GPU spins for about a millisecond ahead of the timed region
