@@ -1417,12 +1417,25 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
     }
     __syncthreads();  // every live pair's y columns are in LDS
     if ((int)threadIdx.x < C) {
+        // Eight pairs at a time: their table entries and y values are read
+        // before the fmaf chain (ascending j, as the blend kernel sums), so
+        // the LDS reads overlap instead of forming one dependent chain.
         const int col = threadIdx.x;
         float acc = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int r = bl->live_of[j];
-            if (r == -2) continue;
-            acc = fmaf(bl->w[j], r >= 0 ? ypart[r * C + col] : 0.f, acc);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int r[8];
+            float wv[8], yv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool in = j0 + u < k;
+                r[u] = in ? bl->live_of[j0 + u] : -2;
+                wv[u] = in ? bl->w[j0 + u] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) yv[u] = r[u] >= 0 ? ypart[r[u] * C + col] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (r[u] != -2) acc = fmaf(wv[u], yv[u], acc);
         }
         a.blend_out[(size_t)t * a.N + col0 + col] = moe::f32_to_bf16_rne(acc);
     }
