@@ -1230,6 +1230,31 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
     const int lane = threadIdx.x & 63, w = moe::wave_id();
     constexpr int D = kDepth;
 
+    // One token: its k routed pairs hold every row of h, so the rows are
+    // loaded in sorted order before the pairs are read (they do not wait
+    // for the positions); a live pair then uses its position's row.  Thread
+    // i of the block loads chunks i, i + 256, ... (8 floats each), as the
+    // staging below does.
+    constexpr int kPreSB = 4;
+    const int cpr = a.K >> 3;
+    const bool pre = gridDim.y == 1 && k * cpr <= kThreads * kPreSB;
+    f32x4_t pf0[kPreSB], pf1[kPreSB];
+    int prow[kPreSB];
+    if (pre) {
+        const float *hsrc = static_cast<const float *>(a.act);
+        const int nch = k * cpr;
+#pragma unroll
+        for (int i = 0; i < kPreSB; ++i) {
+            const int idx = i * kThreads + (int)threadIdx.x;
+            const int ic = idx < nch ? idx : 0;
+            const int m = ic / cpr, kc = ic - m * cpr;
+            prow[i] = m;
+            const float *src = hsrc + (size_t)m * a.K + 8 * kc;
+            pf0[i] = moe::gload<f32x4_t>(src);
+            pf1[i] = moe::gload<f32x4_t>(src + 4);
+        }
+    }
+
     if (w == 0) {  // the token's pairs: lane j holds pair j
         int pos = -1, id = -1;
         float wj = 0.f;
@@ -1321,19 +1346,35 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
             }
         };
 
-        stage<false, true>(
-            a, 0, nlive, nullptr, xs, bl->rmax,
-            [&]() {
-                __builtin_amdgcn_sched_barrier(0);
-                if (nu > 0) {
+        auto fill = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            if (nu > 0) {
 #pragma unroll
-                    for (int d = 0; d < D; ++d) {
-                        load(d);
-                        __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
-                    }
+                for (int d = 0; d < D; ++d) {
+                    load(d);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the ring's issue order
                 }
-            },
-            bl->pos);
+            }
+        };
+        if (pre) {
+            // The preloaded rows: maxima, then scaled to fp16 in sorted order.
+            fill();
+            const int nch = k * cpr;
+#pragma unroll
+            for (int i = 0; i < kPreSB; ++i)
+                if (i * kThreads < nch) row_max_merge(bl->rmax, prow[i], __float_as_uint(absmax8f(pf0[i], pf1[i])));
+            __syncthreads();  // maxima complete
+#pragma unroll
+            for (int i = 0; i < kPreSB; ++i) {
+                const int idx = i * kThreads + (int)threadIdx.x;
+                const int ic = idx < nch ? idx : 0;
+                const int kc = ic - prow[i] * cpr;
+                put_f16x8(xs + prow[i] * ldx + 8 * kc, pf0[i], pf1[i], exp2i(-row_exp(bl->rmax[prow[i]])));
+            }
+            __syncthreads();
+        } else {
+            stage<false, true>(a, 0, nlive, nullptr, xs, bl->rmax, fill, bl->pos);
+        }
 
         if (nu > 0) {
             const int cA = n & 3;
@@ -1352,12 +1393,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
                     *reinterpret_cast<u32x4_t *>(sc_lds + 16 * lane) = r;
                 }
                 const int rl = w + kWaves * (cu < nu ? cp : npw - 1);  // live row of this unit
+                const int xr = pre ? bl->pos[rl] : rl;                 // its staged row
                 const int ka = 512 * ci + 128 * q + 32 * cA;
                 const int kac = ka < K ? ka : 0;
                 f16x8_t a0[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + rl * ldx + kac + 8 * ks);
+                    a0[ks] = *reinterpret_cast<const f16x8_t *>(xs + xr * ldx + kac + 8 * ks);
                 const int kq = 512 * ci + 128 * q + 32 * c;
                 const bool kin = cu < nu && kq < K;
                 const uint8_t *sp = sc_lds + 256 * (d % kGroup) + sread0;
@@ -1382,7 +1424,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
                 if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
                     // Every A row holds the pair's h row: keep token 0 (q == 0)
                     // of the quad sums.
-                    const float oscale = exp2i(row_exp(bl->rmax[rl]));
+                    const float oscale = exp2i(row_exp(bl->rmax[xr]));
                     const float s2 = bl->s2[rl];
                     const float g0 = moe::group_sum<4>(pick(acc0, c)) * oscale;
                     const float g1 = moe::group_sum<4>(pick(acc1, c)) * oscale;
