@@ -1057,6 +1057,12 @@ __device__ __forceinline__ Cursor locate(const DecArgs &a, const int *pre, const
 // (in the area the activation rows use later) and the share's first 64
 // slots move to registers (lane i: slot first + i) before the first pass
 // stages over them.
+// Fused sort in the persistent launch: the sorted tokens sit at this int
+// offset of the pass-prefix area, above its at most kBlockSortPairs + 1
+// entries.
+constexpr int kSortTokPre = moe::kBlockSortPairs + 4;
+static_assert(kSortTokPre + moe::kBlockSortPairs <= kPreLds / 4, "the sorted tokens fit the prefix area");
+
 template <bool GATED, bool SORT>  // SORT: the routing sort runs in every block (P <= 256; block 0 writes it)
 __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     extern __shared__ uint4 lds4[];
@@ -1068,13 +1074,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     const int *tokl = nullptr;
     if constexpr (SORT) {
         // Set-up area (where the activation rows go later): offsets[E + 1],
-        // per-wave histograms [4 E], active list [E], sorted tokens [P],
-        // then the slot cache.
+        // per-wave histograms [4 E], active list [E], then the slot cache.
+        // The sorted tokens go above the pass prefix instead: every pass a
+        // block runs reads its rows' tokens there, also after an earlier
+        // pass's staging has overwritten the set-up area.
         int *offs = reinterpret_cast<int *>(lds + kHdrLds);
         int *cntw = offs + a.E + 1;
         int *act = cntw + 4 * a.E;
-        int *stok = act + a.E;
-        si = reinterpret_cast<SlotInfo *>(stok + a.P);
+        int *stok = pre + kSortTokPre;
+        si = reinterpret_cast<SlotInfo *>(act + a.E);
         const moe::SortOutputs out{a.sort_offsets, a.sort_tok, a.sort_pos, a.sort_active, a.sort_count, a.err_flag};
         n = moe::block_sort_256(a.topk_ids, a.P, a.topk, a.E, offs, cntw, act, stok,
                                 blockIdx.x == 0 ? &out : nullptr);
@@ -1599,11 +1607,12 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     a.cap = cap;
     if (c.persistent) {
         // The set-up caches a SlotInfo per slot where the activation rows go
-        // (with the sort in the launch: after its LDS tables).
+        // (with the sort in the launch: after its LDS tables; the sorted
+        // tokens go above the pass prefix).
         size_t setup = sizeof(SlotInfo) * (size_t)cap;
         const bool sort_here = fuse && decode_sort_fuses(c, P);
         if (sort_here) {
-            setup += sizeof(int) * (size_t)(6 * E + 1 + P);
+            setup += sizeof(int) * (size_t)(6 * E + 1);
             a.P = P;
             a.topk = fuse->k;
             a.E = E;
