@@ -91,10 +91,11 @@ def parse():
     ap.add_argument("--measure", choices=["stream", "transpose"], default=None,
                     help="instead of the step: the streaming-read ceiling over a 4 GiB buffer "
                          "(moe_nvfp4_stream_read), or transpose_u8 over the many-token workload's weights")
-    ap.add_argument("--profile-pass", choices=["gate_up", "down", "copy"], default=None,
+    ap.add_argument("--profile-pass", choices=["gate_up", "down", "down_blend", "copy"], default=None,
                     help="for counter runs under rocprofv3: launch only gate+up+SiLU (after one sort), or "
-                         "only the down projection (after one sort and gate+up), --steps times, or a plain "
-                         "1 GiB device copy --steps times, then exit")
+                         "only the down projection, or only the down projection with the blend fused in "
+                         "(each after one sort and gate+up), --steps times, or a plain 1 GiB device copy "
+                         "--steps times, then exit")
     return ap.parse_args()
 
 
@@ -378,18 +379,21 @@ def measure(args, cfg_id, K, W):
                 dst.copy_(src)
         torch.cuda.synchronize()
         return None
-    if args.profile_pass in ("gate_up", "down"):
+    if args.profile_pass in ("gate_up", "down", "down_blend"):
         with torch.cuda.stream(stream):
             sort_launch(stream)
-            if args.profile_pass == "down":
+            if args.profile_pass != "gate_up":
                 gate_up_launch(0, stream)
             for i in range(args.steps):
+                dn = layers[i % L][1][2]
                 if args.profile_pass == "gate_up":
                     gate_up_launch(i, stream)
-                else:
-                    dn = layers[i % L][1][2]
+                elif args.profile_pass == "down":
                     moe.moe_nvfp4_down(bufs.h, shape.T, shape.k, shape.E, shape.H, shape.I, dn,
                                        bufs.expert_offsets, bufs.active_experts, bufs.active_count, bufs.y, stream)
+                else:
+                    moe.moe_nvfp4_down_blend(bufs.h, ids_d[0], w_d[0], bufs.pair_pos, shape.E, shape.H, shape.I, dn,
+                                             bufs.out, stream)
         torch.cuda.synchronize()
         return None
 

@@ -1202,7 +1202,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
 //     ascending j.  Live pair r belongs to wave r mod 4.
 //   * Activations.  The h rows of the live pairs (gathered by sorted
 //     position) are staged as in the grouped kernel: fp16, one power of two
-//     per row.
+//     per row.  With one token every row of h is one of its pairs', so the
+//     rows are loaded at entry in sorted order, before the pairs are read.
 //   * Stream.  Wave w streams units of 8 weight rows, (its p-th live pair,
 //     column group g), through the same register ring, lane layout and
 //     matrix-core arithmetic as the grouped kernel, so each y value is the
