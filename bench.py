@@ -18,20 +18,21 @@ decode workload (the top-level fields) and the 32-token decode workload
 workload alone.
 
 The K timed steps are captured into one HIP graph.  It is replayed once
-untimed (the first replay of a graph also uploads it), then a 1 GiB buffer
-is read through once to evict the caches, the W warm-up steps (other weight
-copies than the timed ones) run once more, every routing batch's inputs
-(x, expert ids, weights) are read once, as the router and the previous
-layer would just have written them, and the timed replay runs between a
-device synchronisation on each side (``--eager`` launches the
-steps one by one instead).  The eviction reads rather than writes: a
-rewritten buffer left the Infinity Cache full of dirty lines, whose write-
-back slowed the first dozen steps after it (a 20-step replay of the 1-token
-step measured 20.0 us per step against 17.1 us over 2000 steps; with the
-read and the warm-up replay, 18.0 us).  A one-wave spin kernel of about a millisecond runs just ahead
-of the start event, so that the host has submitted the replay before the
-timed region opens (otherwise a fixed submission latency of the order of
-50 us lands in it, a few percent of a 20-step replay).  Reported on one JSON line, per workload:
+untimed (the first replay of a graph also uploads it).  Then, queued back
+to back behind a one-wave spin kernel of about a millisecond (which covers
+the host's submission of everything after it): a 1 GiB buffer read once
+through the streaming-read kernel to evict the caches, the W warm-up steps
+again (other weight copies than the timed ones), one read of every routing
+batch's inputs (x, expert ids, weights, as the router and the previous
+layer would just have written them), the start event, the timed replay and
+the end event (``--eager`` launches the steps one by one instead).  The
+eviction reads rather than writes: a rewritten buffer left the Infinity
+Cache full of dirty lines, whose write-back slowed the first dozen steps
+after it (a 20-step replay of the 1-token step measured 20.0 us per step
+against 17.1 us over 2000 steps; with the read and the warm-up replay,
+18.0 us).  ``--warm-cache`` (context only, labelled in config.cache) keeps
+one weight copy and skips the eviction.  Reported on one JSON line, per
+workload:
   value       expert-weight bytes of the active experts per step / step time (GB/s)
   tokens_per_s, pct_of_hbm_peak
   dtype       the arithmetic: f16 (decode: fp16 matrix-core operands, fp32
@@ -44,6 +45,9 @@ timed region opens (otherwise a fixed submission latency of the order of
               2.5 PFLOP/s fp16/bf16 matrix-core peak); traffic = HBM bytes per
               launch from the committed counter summary in profiles/ while
               the kernel sources are unchanged since it was taken, else null
+  projection_launches  the down launch the step runs (HIP events, as for
+              roofline) and the expert-weight bytes over the gate+up and down
+              launch times alone (sort, blend and launch gaps excluded)
   router      launch time of moe_nvfp4_route on the workload's logits (the
               router ahead of the path; not part of the step)
   cpu_baseline the fp64 oracle on the host cores for a bounded sample of the
@@ -86,6 +90,9 @@ def parse():
                     help="expert weight format (mxfp4: K-major workloads only)")
     ap.add_argument("--gate-up", choices=["separate", "concat"], default="separate",
                     help="gate and up as two K-major twins, or one concatenated twin (K-major workloads only)")
+    ap.add_argument("--warm-cache", action="store_true",
+                    help="context only, labelled as such: one weight copy and no cache eviction, so the step "
+                         "reads its weights from wherever the caches hold them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--measure", choices=["stream", "transpose"], default=None,
@@ -310,7 +317,9 @@ def measure(args, cfg_id, K, W):
     w_d = [torch.from_numpy(w).to(dev) for w in ws]
     step_bytes = [active_weight_bytes(shape, i, group) for i in idss]
     all_bytes = shape.E * synth.expert_bytes(shape, group)
-    if args.layers > 0:
+    if args.warm_cache:
+        L = 1
+    elif args.layers > 0:
         L = args.layers
     else:
         L = max(1, math.ceil(2.0e9 / min(step_bytes)))
@@ -413,7 +422,8 @@ def measure(args, cfg_id, K, W):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     if args.eager:
-        flush_caches(dev)
+        if not args.warm_cache:
+            flush_caches(dev)
         with torch.cuda.stream(stream):
             run_steps(0, W, stream)
         touch_inputs(xs + ids_d + w_d)
@@ -444,7 +454,8 @@ def measure(args, cfg_id, K, W):
             # graph, so these run back to back and the timed region holds
             # the K steps, not the submission latency of the replay.
             torch.cuda._sleep(SPIN_CYCLES)
-            flush_caches(dev)
+            if not args.warm_cache:
+                flush_caches(dev)
             g_warm.replay()
             touch_inputs(xs + ids_d + w_d)
             t_start.record(stream)
@@ -489,6 +500,30 @@ def measure(args, cfg_id, K, W):
     roof.update({"traffic": traffic, "kernel": kname, "launch_us": round(gu_ms * 1e3, 3),
                  "algorithmic_bytes_per_launch": round(gu_bytes)})
 
+    # ---- the down launch the step runs (with the blend fused in at one
+    # token with row-major weights), timed the same way after one gate+up.
+    fused_blend = shape.T == 1 and not shape.kmajor
+    with torch.cuda.stream(stream):
+        gate_up_launch(0, stream)
+        for rep in range(2):
+            e0.record(stream)
+            for i in range(Kr):
+                dn = layers[i % L][1][2]
+                if fused_blend:
+                    moe.moe_nvfp4_down_blend(bufs.h, ids_d[0], w_d[0], bufs.pair_pos, shape.E, shape.H, shape.I, dn,
+                                             bufs.out, stream)
+                else:
+                    moe.moe_nvfp4_down(bufs.h, shape.T, shape.k, shape.E, shape.H, shape.I, dn, bufs.expert_offsets,
+                                       bufs.active_experts, bufs.active_count, bufs.y, stream)
+            e1.record(stream)
+    torch.cuda.synchronize()
+    dn_ms = e0.elapsed_time(e1) / Kr
+    # Expert-weight bytes over the two projection launches alone (sort,
+    # blend and launch gaps excluded), beside value's whole-step rate.
+    kernels = {"down_kernel": "moe_nvfp4_down_blend (blend fused in)" if fused_blend else "moe_nvfp4_down",
+               "down_launch_us": round(dn_ms * 1e3, 3),
+               "weight_GBps_over_gate_up_and_down_launches": round(step_bytes[0] / ((gu_ms + dn_ms) / 1e3) / 1e9, 1)}
+
     # ---- the router ahead of the path (softmax, top-k, renormalise), timed
     # on its own over the workload's logits; it is not part of the step.
     logits_d = torch.from_numpy(synth.gen_logits(cfg_id, shape)).to(dev)
@@ -518,11 +553,13 @@ def measure(args, cfg_id, K, W):
             "weight_format": args.format, "gate_up_twin": args.gate_up if shape.kmajor else "row_major",
             "weight_copies_cycled": L, "routing_batches_cycled": R,
             "launch": "eager" if args.eager else "hip_graph",
+            "cache": "warm (one weight copy, no eviction)" if args.warm_cache else "cold (weights from HBM)",
         },
         "tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "active_weight_bytes_per_step": round(bytes_timed / K),
         "roofline": roof,
+        "projection_launches": kernels,
         "router": router,
         "cpu_baseline": None,
     }
