@@ -182,10 +182,13 @@ __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ float absmax8(uint4 v) {
-    const float a = fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
-    const float b = fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
-    return fmaxf(a, b);
+// Largest magnitude of 8 bf16 values, as two 16-bit halves: with the sign
+// bit cleared, bf16 bits order as their magnitudes do (NaN above inf).
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+__device__ __forceinline__ u16x2_t absmax8_bf16(uint4 v) {
+    auto m = [](uint32_t u) { return __builtin_bit_cast(u16x2_t, u & 0x7fff7fffu); };
+    return __builtin_elementwise_max(__builtin_elementwise_max(m(v.x), m(v.y)),
+                                     __builtin_elementwise_max(m(v.z), m(v.w)));
 }
 
 __device__ __forceinline__ float absmax8f(const f32x4_t &a, const f32x4_t &b) {
@@ -205,20 +208,21 @@ __device__ __forceinline__ void put_f16x8(uint16_t *dst, const f32x4_t &a, const
     *reinterpret_cast<f16x8_t *>(dst) = h;
 }
 
-// Max-merge v (a non-negative float's bits) into rmax[m] for the 64 lanes of
-// a wave holding consecutive chunks, so m takes at most a few consecutive
-// values: the first and the last lane's rows get one atomic each after a wave
-// reduction; lanes of any row strictly between (short rows only) post their
-// own.
-__device__ __forceinline__ void row_max_merge(uint32_t *rmax, int m, uint32_t v) {
+// Row maxima with 2^lgt threads per row (lgt >= 2): the groups are
+// aligned runs of lanes, so a row's threads share a wave (up to 16 lanes)
+// or span whole 16-lane runs.  v is a non-negative float's bits; each run's
+// first lane merges the run's maximum into rmax[m] (rows m < pr only).
+__device__ __forceinline__ uint32_t threads_per_row_log2(int rows) {  // rows <= 64: 2^lgt >= 4
+    return rows <= 1 ? 8u : 8u - (32u - (uint32_t)__builtin_clz((uint32_t)(rows - 1)));
+}
+__device__ __forceinline__ void row_group_max(uint32_t *rmax, int m, bool in, uint32_t v, int lgt) {
     const int lane = threadIdx.x & 63;
-    const int m_lo = __builtin_amdgcn_readfirstlane(m);
-    const int m_hi = __builtin_amdgcn_readlane(m, 63);
-    const uint32_t lo = moe::wave_max_u32(m == m_lo ? v : 0u);
-    const uint32_t hi = moe::wave_max_u32(m == m_hi ? v : 0u);
-    if (lane == 0) atomicMax(rmax + m_lo, lo);
-    if (lane == 63 && m_hi != m_lo) atomicMax(rmax + m_hi, hi);
-    if (m != m_lo && m != m_hi) atomicMax(rmax + m, v);
+    v = max(v, moe::dpp_u32<moe::kDppXor1>(v));
+    v = max(v, moe::dpp_u32<moe::kDppXor2>(v));
+    if (lgt >= 3) v = max(v, moe::dpp_u32<moe::kDppHalfMirror>(v));
+    if (lgt >= 4) v = max(v, moe::dpp_u32<moe::kDppMirror>(v));
+    const int run = lgt >= 4 ? 15 : (1 << lgt) - 1;
+    if (in && (lane & run) == 0) atomicMax(rmax + m, v);
 }
 
 // Stage rows [row0, row0 + pr) of the activation into LDS as fp16 (stride
@@ -235,10 +239,9 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
     const int K = a.K, ldx = a.ldx;
     auto hrow = [&](int m) -> size_t { return GATHER ? (size_t)gpos[m] : (size_t)(row0 + m); };
     const int cpr = K >> 3;  // 8-element chunks per row
-    const int nch = pr * cpr;
     constexpr int SB = 4;  // h: chunks per thread per batch
-    // Unconditional LDS writes throughout: a chunk past the end re-writes
-    // chunk 0 with its own value, and no load is left in flight on any path.
+    // pr <= 64 rows.  No load sits behind a branch, so none is left in
+    // flight on any path.
     if constexpr (GATED) {
         // x rows (bf16 bytes) straight into their LDS slots by direct loads,
         // issued ahead of the weight ring (mid()): loads complete in issue
@@ -250,114 +253,111 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
         const int nslot = pr * spr;
         const int lane = threadIdx.x & 63, w = moe::wave_id();
         uint8_t *xb = reinterpret_cast<uint8_t *>(xs);
+        // Slot base + lane is chunk kc of row m; both advance by the slot
+        // stride without a division per load.
+        int m = (64 * w + lane) / spr, kc = 64 * w + lane - m * spr;
         for (int base = 64 * w; base < nslot; base += 64 * kWaves) {
-            const int sl = base + lane;
-            const int m = sl / spr, kc = sl - m * spr;
             const int tok = ptok[m < pr ? m : 0];
-            if (sl < nslot)
+            if (base + lane < nslot)
                 __builtin_amdgcn_global_load_lds(
                     (const MOE_GLOBAL void *)(x + (size_t)tok * K + 8 * (kc < cpr ? kc : 0)),
                     (MOE_LDS void *)(xb + 16 * base), 16, 0, 0);
+            kc += 64 * kWaves;
+            while (kc >= spr) {
+                kc -= spr;
+                ++m;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         mid();
         __builtin_amdgcn_s_waitcnt(moe::waitcnt_vm(kRingFillLoads));  // this wave's x slots have landed
         moe::lds_barrier();
-        // Row maxima (lanes of a wave hold consecutive chunks; past the end,
-        // chunk 0 again).
-        for (int base = 0; base < nch; base += kThreads) {
-            const int idx = base + (int)threadIdx.x;
-            const int ic = idx < nch ? idx : 0;
-            const int m = ic / cpr, kc = ic - m * cpr;
-            const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * ldx + 8 * kc);
-            row_max_merge(rmax, m, __float_as_uint(absmax8(v)));
-        }
+        // Maxima and conversion: 2^lgt threads per row, thread t on row
+        // t >> lgt and every 2^lgt-th chunk of it from t mod 2^lgt.
+        const int lgt = (int)threads_per_row_log2(pr);
+        const int tm = (int)threadIdx.x >> lgt, tj = (int)threadIdx.x & ((1 << lgt) - 1);
+        const bool rin = tm < pr;
+        uint16_t *xr = xs + (rin ? tm : 0) * ldx;
+        u16x2_t mx = {0, 0};
+        if (rin)
+            for (int c = tj; c < cpr; c += 1 << lgt)
+                mx = __builtin_elementwise_max(mx, absmax8_bf16(*reinterpret_cast<const uint4 *>(xr + 8 * c)));
+        // float bits of the largest magnitude
+        row_group_max(rmax, tm, rin, (uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16, lgt);
         moe::lds_barrier();  // maxima complete
-        for (int idx = threadIdx.x; idx < nch; idx += kThreads) {  // bf16 -> scaled fp16 in place
-            const int m = idx / cpr, kc = idx - m * cpr;
-            const float f = exp2i(-row_exp(rmax[m]));
-            uint4 *p = reinterpret_cast<uint4 *>(xs + m * ldx + 8 * kc);
-            const uint4 v = *p;
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-            f16x8_t h;
+        if (rin) {  // bf16 -> scaled fp16 in place
+            const float f = exp2i(-row_exp(rmax[tm]));
+            for (int c = tj; c < cpr; c += 1 << lgt) {
+                uint4 *p = reinterpret_cast<uint4 *>(xr + 8 * c);
+                const uint4 v = *p;
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+                f16x8_t h;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                h[2 * i] = (_Float16)(bf16_lo(u[i]) * f);
-                h[2 * i + 1] = (_Float16)(bf16_hi(u[i]) * f);
+                for (int i = 0; i < 4; ++i) {
+                    h[2 * i] = (_Float16)(bf16_lo(u[i]) * f);
+                    h[2 * i + 1] = (_Float16)(bf16_hi(u[i]) * f);
+                }
+                *reinterpret_cast<f16x8_t *>(p) = h;
             }
-            *reinterpret_cast<f16x8_t *>(p) = h;
         }
         moe::lds_barrier();
     } else {
         const float *h = static_cast<const float *>(a.act);
-        auto chunk = [&](int idx, int &m, int &kc) {
-            const int ic = idx < nch ? idx : 0;
-            m = ic / cpr;
-            kc = ic - m * cpr;
+        // 2^lgt threads per row, thread t on row t >> lgt and its chunks
+        // t mod 2^lgt + 2^lgt i.  Every thread issues the same loads (a chunk
+        // past its row's end, or a thread past the last row, re-reads a valid
+        // chunk that is not used), so the ring's waits stay exact.
+        const int lgt = (int)threads_per_row_log2(pr);
+        const int tm = (int)threadIdx.x >> lgt, tj = (int)threadIdx.x & ((1 << lgt) - 1);
+        const bool rin = tm < pr;
+        const float *src = h + hrow(rin ? tm : 0) * K;
+        uint16_t *dst = xs + (rin ? tm : 0) * ldx;
+        const int nct = (cpr + (1 << lgt) - 1) >> lgt;  // chunks per thread, at most
+        auto ld = [&](int i, f32x4_t &f0, f32x4_t &f1) {
+            const int c = min(tj + (i << lgt), cpr - 1);
+            f0 = moe::gload<f32x4_t>(src + 8 * c);
+            f1 = moe::gload<f32x4_t>(src + 8 * c + 4);
         };
-        if (nch <= kThreads * SB) {
+        auto valid = [&](int i) { return rin && tj + (i << lgt) < cpr; };
+        uint32_t mx = 0u;
+        if (nct <= SB) {
             // One batch: the rows stay in registers between the two phases.
-            int row[SB];
             f32x4_t f0[SB], f1[SB];
 #pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                int m, kc;
-                chunk(i * kThreads + (int)threadIdx.x, m, kc);
-                row[i] = m;
-                const float *src = h + hrow(m) * K + 8 * kc;
-                f0[i] = moe::gload<f32x4_t>(src);
-                f1[i] = moe::gload<f32x4_t>(src + 4);
-            }
+            for (int i = 0; i < SB; ++i) ld(i, f0[i], f1[i]);
             mid();
 #pragma unroll
             for (int i = 0; i < SB; ++i)
-                if (i * kThreads < nch) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+                if (valid(i)) mx = max(mx, __float_as_uint(absmax8f(f0[i], f1[i])));
+            row_group_max(rmax, tm, rin, mx, lgt);
             __syncthreads();  // maxima complete
+            const float f = exp2i(-row_exp(rmax[rin ? tm : 0]));
 #pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int idx = i * kThreads + (int)threadIdx.x;
-                const int ic = idx < nch ? idx : 0;
-                const int kc = ic - row[i] * cpr;
-                put_f16x8(xs + row[i] * ldx + 8 * kc, f0[i], f1[i], exp2i(-row_exp(rmax[row[i]])));
-            }
+            for (int i = 0; i < SB; ++i)
+                if (valid(i)) put_f16x8(dst + 8 * (tj + (i << lgt)), f0[i], f1[i], f);
         } else {
             // Several batches: maxima first, then the rows read again (L2 hits).
-            auto batch = [&](int base, auto first) {
-                int row[SB];
+            auto batch = [&](int b, auto first) {
                 f32x4_t f0[SB], f1[SB];
 #pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    int m, kc;
-                    chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
-                    row[i] = m;
-                    const float *src = h + hrow(m) * K + 8 * kc;
-                    f0[i] = moe::gload<f32x4_t>(src);
-                    f1[i] = moe::gload<f32x4_t>(src + 4);
-                }
+                for (int i = 0; i < SB; ++i) ld(b + i, f0[i], f1[i]);
                 if constexpr (decltype(first)::value) mid();
 #pragma unroll
                 for (int i = 0; i < SB; ++i)
-                    if (base + i * kThreads < nch) row_max_merge(rmax, row[i], __float_as_uint(absmax8f(f0[i], f1[i])));
+                    if (valid(b + i)) mx = max(mx, __float_as_uint(absmax8f(f0[i], f1[i])));
             };
             batch(0, std::true_type{});
-            for (int base = kThreads * SB; base < nch; base += kThreads * SB) batch(base, std::false_type{});
+            for (int b = SB; b < nct; b += SB) batch(b, std::false_type{});
+            row_group_max(rmax, tm, rin, mx, lgt);
             __syncthreads();  // maxima complete
-            for (int base = 0; base < nch; base += kThreads * SB) {
-                int dst[SB];
-                float fs[SB];
+            const float f = exp2i(-row_exp(rmax[rin ? tm : 0]));
+            for (int b = 0; b < nct; b += SB) {
                 f32x4_t f0[SB], f1[SB];
 #pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    int m, kc;
-                    chunk(base + i * kThreads + (int)threadIdx.x, m, kc);
-                    dst[i] = m * ldx + 8 * kc;
-                    fs[i] = exp2i(-row_exp(rmax[m]));
-                    const float *src = h + hrow(m) * K + 8 * kc;
-                    f0[i] = moe::gload<f32x4_t>(src);
-                    f1[i] = moe::gload<f32x4_t>(src + 4);
-                }
+                for (int i = 0; i < SB; ++i) ld(b + i, f0[i], f1[i]);
 #pragma unroll
-                for (int i = 0; i < SB; ++i) put_f16x8(xs + dst[i], f0[i], f1[i], fs[i]);
+                for (int i = 0; i < SB; ++i)
+                    if (valid(b + i)) put_f16x8(dst + 8 * (tj + ((b + i) << lgt)), f0[i], f1[i], f);
             }
         }
         __syncthreads();
@@ -1241,26 +1241,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
 
     // One token: its k routed pairs hold every row of h, so the rows are
     // loaded in sorted order before the pairs are read (they do not wait
-    // for the positions); a live pair then uses its position's row.  Thread
-    // i of the block loads chunks i, i + 256, ... (8 floats each), as the
-    // staging below does.
+    // for the positions); a live pair then uses its position's row.  The
+    // threads split the rows as the staging below does: 2^plg threads per
+    // row, thread i on row i >> plg and its chunks (8 floats each)
+    // i mod 2^plg + 2^plg j.
     constexpr int kPreSB = 4;
     const int cpr = a.K >> 3;
-    const bool pre = gridDim.y == 1 && k * cpr <= kThreads * kPreSB;
+    const int plg = k <= 64 ? (int)threads_per_row_log2(k) : 2;
+    const int pm = (int)threadIdx.x >> plg, pj = (int)threadIdx.x & ((1 << plg) - 1);
+    const bool pre = gridDim.y == 1 && k <= 64 && ((cpr + (1 << plg) - 1) >> plg) <= kPreSB;
     f32x4_t pf0[kPreSB], pf1[kPreSB];
-    int prow[kPreSB];
     if (pre) {
-        const float *hsrc = static_cast<const float *>(a.act);
-        const int nch = k * cpr;
+        const float *hsrc = static_cast<const float *>(a.act) + (size_t)(pm < k ? pm : 0) * a.K;
 #pragma unroll
         for (int i = 0; i < kPreSB; ++i) {
-            const int idx = i * kThreads + (int)threadIdx.x;
-            const int ic = idx < nch ? idx : 0;
-            const int m = ic / cpr, kc = ic - m * cpr;
-            prow[i] = m;
-            const float *src = hsrc + (size_t)m * a.K + 8 * kc;
-            pf0[i] = moe::gload<f32x4_t>(src);
-            pf1[i] = moe::gload<f32x4_t>(src + 4);
+            const int c = min(pj + (i << plg), cpr - 1);
+            pf0[i] = moe::gload<f32x4_t>(hsrc + 8 * c);
+            pf1[i] = moe::gload<f32x4_t>(hsrc + 8 * c + 4);
         }
     }
 
@@ -1368,18 +1365,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_down_blend(DecArgs a) {
         if (pre) {
             // The preloaded rows: maxima, then scaled to fp16 in sorted order.
             fill();
-            const int nch = k * cpr;
+            const bool rin = pm < k;
+            uint32_t mx = 0u;
 #pragma unroll
             for (int i = 0; i < kPreSB; ++i)
-                if (i * kThreads < nch) row_max_merge(bl->rmax, prow[i], __float_as_uint(absmax8f(pf0[i], pf1[i])));
+                if (rin && pj + (i << plg) < cpr) mx = max(mx, __float_as_uint(absmax8f(pf0[i], pf1[i])));
+            row_group_max(bl->rmax, pm, rin, mx, plg);
             __syncthreads();  // maxima complete
+            const float f = exp2i(-row_exp(bl->rmax[rin ? pm : 0]));
 #pragma unroll
-            for (int i = 0; i < kPreSB; ++i) {
-                const int idx = i * kThreads + (int)threadIdx.x;
-                const int ic = idx < nch ? idx : 0;
-                const int kc = ic - prow[i] * cpr;
-                put_f16x8(xs + prow[i] * ldx + 8 * kc, pf0[i], pf1[i], exp2i(-row_exp(bl->rmax[prow[i]])));
-            }
+            for (int i = 0; i < kPreSB; ++i)
+                if (rin && pj + (i << plg) < cpr) put_f16x8(xs + pm * ldx + 8 * (pj + (i << plg)), pf0[i], pf1[i], f);
             __syncthreads();
         } else {
             stage<false, true>(a, 0, nlive, nullptr, xs, bl->rmax, fill, bl->pos);
