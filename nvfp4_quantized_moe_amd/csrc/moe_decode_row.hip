@@ -946,13 +946,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     }
 }
 
-// Relative cost of one unit of a pass with r routed rows (token groups of 4
-// share each decoded weight; the weight stream itself costs the same).
-// (A flatter model fitted to per-block timestamps, 12 + ceil(r / 4),
-// measured 2-3% slower on the 32- and 64-token launches.)
-constexpr int kUnitCostMax = 7;  // unit_cost(16)
+// Relative cost of one unit of a pass with r routed rows, for the share
+// walk (token groups of 4 share each decoded weight; the weight stream
+// itself costs the same).  On the 64-token launch the flatter model below
+// measured 3% slower here.
+constexpr int kUnitCostMax = 35;  // the larger of unit_cost(16) and unit_cost_one(16)
 constexpr int kOnePassShares = 4;  // one pass per block when every pass is worth this many shares
 __device__ __forceinline__ int unit_cost(int r) { return 3 + ((r + 3) >> 2); }
+// The same for one pass per block: fitted to per-block timestamps of the
+// 32-token launch (staging, then about 3.6 + 0.07 r us per unit), where it
+// brings the blocks' ends closer together than unit_cost (launch 3%
+// shorter).
+__device__ __forceinline__ int unit_cost_one(int r) { return 19 + r; }
 
 // An active slot's expert, first sorted position and routed rows, cached in
 // LDS while a persistent block finds its share.
@@ -962,16 +967,17 @@ struct SlotInfo {
 
 // Block-wide: every slot's expert and row range (slot(sl) for sl < cap,
 // an expert of -1 past the active count), cached in si[sl]; and the
-// exclusive prefix sum over the n active slots of the cost of all their
-// passes (units x unit_cost per pass): pre[s] for s < n, pre[n] = total.
-// pass_min: the cost of the cheapest pass.
+// exclusive prefix sums over the n active slots of the cost of all their
+// passes (units x unit_cost per pass in pre, units x unit_cost_one in
+// pre1): pre[s] for s < n, pre[n] = total (the same for pre1).  pass_min:
+// the unit_cost cost of the cheapest pass.
 template <typename SlotFn>
-__device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre, SlotInfo *si, int &pass_min,
-                                            SlotFn &&slot) {
-    __shared__ int wsum[kWaves], wmin[kWaves];
+__device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre, int *pre1, SlotInfo *si,
+                                            int &pass_min, SlotFn &&slot) {
+    __shared__ int wsum[2][kWaves], wmin[kWaves];
     const int t = threadIdx.x, lane = t & 63, w = moe::wave_id();
     const int pr = a.pass_rows, cap = a.cap;
-    int c[4], sum = 0, cmin = 0x7fffffff;
+    int c[4], c1[4], sum = 0, sum1 = 0, cmin = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * t + i;
@@ -979,31 +985,49 @@ __device__ __forceinline__ void cost_prefix(const DecArgs &a, int n, int *pre, S
         const int r = in.rows;
         if (sl < cap) si[sl] = in;
         const int full = r / pr, rem = r - full * pr;
-        const int cost = sl < n ? a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0)) : 0;
-        c[i] = cost;
-        sum += cost;
-        if (sl < n) cmin = min(cmin, a.units * unit_cost(rem > 0 ? rem : pr));  // the slot's cheapest pass
+        const bool act = sl < n;
+        c[i] = act ? a.units * (full * unit_cost(pr) + (rem > 0 ? unit_cost(rem) : 0)) : 0;
+        c1[i] = act ? a.units * (full * unit_cost_one(pr) + (rem > 0 ? unit_cost_one(rem) : 0)) : 0;
+        sum += c[i];
+        sum1 += c1[i];
+        if (act) cmin = min(cmin, a.units * unit_cost(rem > 0 ? rem : pr));  // the slot's cheapest pass
     }
-    int incl = sum;
+    int incl = sum, incl1 = sum1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
+        const int v = __shfl_up(incl, off, 64), v1 = __shfl_up(incl1, off, 64);
+        if (lane >= off) {
+            incl += v;
+            incl1 += v1;
+        }
     }
     const uint32_t wm = moe::wave_min_u32((uint32_t)cmin);
-    if (lane == 63) wsum[w] = incl;
+    if (lane == 63) {
+        wsum[0][w] = incl;
+        wsum[1][w] = incl1;
+    }
     if (lane == 0) wmin[w] = (int)wm;
     __syncthreads();
-    int base = 0;
-    for (int i = 0; i < w; ++i) base += wsum[i];
-    int run = base + incl - sum;
+    int base = 0, base1 = 0;
+    for (int i = 0; i < w; ++i) {
+        base += wsum[0][i];
+        base1 += wsum[1][i];
+    }
+    int run = base + incl - sum, run1 = base1 + incl1 - sum1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int sl = 4 * t + i;
-        if (sl < n) pre[sl] = run;
+        if (sl < n) {
+            pre[sl] = run;
+            pre1[sl] = run1;
+        }
         run += c[i];
+        run1 += c1[i];
     }
-    if (t == kThreads - 1) pre[n] = run;
+    if (t == kThreads - 1) {
+        pre[n] = run;
+        pre1[n] = run1;
+    }
     pass_min = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
     __syncthreads();
 }
@@ -1071,6 +1095,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
     const int lane = threadIdx.x & 63;
     int pass_min, n;
     SlotInfo *si;
+    int *pre1;  // prefix of the one-pass-per-block costs, after the slot cache
     const int *tokl = nullptr;
     if constexpr (SORT) {
         // Set-up area (where the activation rows go later): offsets[E + 1],
@@ -1083,20 +1108,22 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         int *act = cntw + 4 * a.E;
         int *stok = pre + kSortTokPre;
         si = reinterpret_cast<SlotInfo *>(act + a.E);
+        pre1 = reinterpret_cast<int *>(si + a.cap);
         const moe::SortOutputs out{a.sort_offsets, a.sort_tok, a.sort_pos, a.sort_active, a.sort_count, a.err_flag};
         n = moe::block_sort_256(a.topk_ids, a.P, a.topk, a.E, offs, cntw, act, stok,
                                 blockIdx.x == 0 ? &out : nullptr);
         tokl = stok;
-        cost_prefix(a, n, pre, si, pass_min, [&](int sl) {
+        cost_prefix(a, n, pre, pre1, si, pass_min, [&](int sl) {
             const int e = sl < n ? act[sl] : -1;
             return e < 0 ? SlotInfo{-1, 0, 0} : SlotInfo{e, offs[e], offs[e + 1] - offs[e]};
         });
     } else {
         si = reinterpret_cast<SlotInfo *>(lds + kHdrLds);
+        pre1 = reinterpret_cast<int *>(si + a.cap);
         // The active list is read without waiting for the active count:
         // its entries past the count are -1.
         n = *a.nactive;
-        cost_prefix(a, n, pre, si, pass_min, [&](int sl) {
+        cost_prefix(a, n, pre, pre1, si, pass_min, [&](int sl) {
             const int e = a.active[sl];
             if (e < 0) return SlotInfo{-1, 0, 0};
             const int lo = a.offsets[e];
@@ -1117,22 +1144,24 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         // it.  Each block then stages once and streams one pass.  (With
         // fewer shares per pass the whole-block rounding unbalances more
         // than a second pass costs: the 64-token launch, about two shares
-        // per pass, measured 8% slower this way.)
-        const int64_t pt = ((int64_t)(2 * bx + 1) * total) / (2 * (int64_t)g);
-        const int sl = find_slot(pre, n, (int)pt);
+        // per pass, measured 8% slower this way.)  The points are placed on
+        // the unit_cost_one prefix.
+        const int total1 = pre1[n];
+        const int64_t pt = ((int64_t)(2 * bx + 1) * total1) / (2 * (int64_t)g);
+        const int sl = find_slot(pre1, n, (int)pt);
         const SlotInfo in = si[sl];
         const int pr = a.pass_rows;
-        int64_t ps = pre[sl];
+        int64_t ps = pre1[sl];
         int p = 0, pc = 0;
         for (;; ++p) {
-            pc = a.units * unit_cost(min(pr, in.rows - p * pr));
+            pc = a.units * unit_cost_one(min(pr, in.rows - p * pr));
             if (pt < ps + pc || (p + 1) * pr >= in.rows) break;
             ps += pc;
         }
-        // blocks whose points lie in [ps, ps + pc): (2b + 1) total in [2 g ps, 2 g (ps + pc))
+        // blocks whose points lie in [ps, ps + pc): (2b + 1) total1 in [2 g ps, 2 g (ps + pc))
         auto first_at = [&](int64_t c) -> int64_t {
-            const int64_t v = 2 * (int64_t)g * c - total;
-            return v <= 0 ? 0 : (v + 2 * (int64_t)total - 1) / (2 * (int64_t)total);
+            const int64_t v = 2 * (int64_t)g * c - total1;
+            return v <= 0 ? 0 : (v + 2 * (int64_t)total1 - 1) / (2 * (int64_t)total1);
         };
         const int b_lo = (int)first_at(ps), nb = (int)(first_at(ps + pc) - b_lo);
         const int i = bx - b_lo;
@@ -1605,8 +1634,8 @@ int moe_launch_decode_row(bool gated, const void *act, const int32_t *sorted_tok
     if (c.persistent) {
         // The set-up caches a SlotInfo per slot where the activation rows go
         // (with the sort in the launch: after its LDS tables; the sorted
-        // tokens go above the pass prefix).
-        size_t setup = sizeof(SlotInfo) * (size_t)cap;
+        // tokens go above the pass prefix), then the one-pass cost prefix.
+        size_t setup = sizeof(SlotInfo) * (size_t)cap + sizeof(int) * (size_t)(cap + 1);
         const bool sort_here = fuse && decode_sort_fuses(c, P);
         if (sort_here) {
             setup += sizeof(int) * (size_t)(6 * E + 1);
