@@ -231,7 +231,9 @@ __device__ __forceinline__ void row_group_max(uint32_t *rmax, int m, bool in, ui
 // gathers x rows by token (row m's token in ptok[m], LDS); down reads h rows
 // in order, or (GATHER) row gpos[m] for row m.
 // mid() issues the weight ring: gate+up after every x load (mid() must issue
-// exactly kRingFillLoads loads), down once the first h loads are in flight.
+// exactly kRingFillLoads loads); down once the first h loads are in flight
+// (rows read in one batch) or once the maxima are known and the first two
+// conversion batches are in flight (rows read in several).
 // Ends with the rows visible to the whole block.
 template <bool GATED, bool GATHER = false, typename Mid>
 __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const int *ptok, uint16_t *xs,
@@ -246,26 +248,34 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
         // x rows (bf16 bytes) straight into their LDS slots by direct loads,
         // issued ahead of the weight ring (mid()): loads complete in issue
         // order, so waiting for x then waits for no weight load.  One 16-byte
-        // slot per lane, 64 consecutive slots of the padded rows per
-        // instruction; a pad slot loads its row's first chunk (never read).
+        // slot per lane, 64 consecutive slots of one padded row per
+        // instruction (a pad slot loads its row's first chunk, never read).
+        // The (row, 64-slot group) items go round-robin over the waves; each
+        // wave holds the pass's tokens in one register (lane r: row r,
+        // pr <= 16) and picks an item's token with a lane read, so no item
+        // waits on a memory read.
         const uint16_t *x = static_cast<const uint16_t *>(a.act);
-        const int spr = ldx >> 3;  // 16-byte slots per staged row (chunks and pad)
-        const int nslot = pr * spr;
+        const int spr = ldx >> 3;          // 16-byte slots per staged row (chunks and pad)
+        const int nit = (spr + 63) >> 6;   // 64-slot groups per row
         const int lane = threadIdx.x & 63, w = moe::wave_id();
         uint8_t *xb = reinterpret_cast<uint8_t *>(xs);
-        // Slot base + lane is chunk kc of row m; both advance by the slot
-        // stride without a division per load.
-        int m = (64 * w + lane) / spr, kc = 64 * w + lane - m * spr;
-        for (int base = 64 * w; base < nslot; base += 64 * kWaves) {
-            const int tok = ptok[m < pr ? m : 0];
-            if (base + lane < nslot)
+        const int tokv = ptok[lane & 15];
+        int row = 0, i = w;  // item w: group i of row `row`
+        while (i >= nit) {
+            i -= nit;
+            ++row;
+        }
+        for (; row < pr;) {
+            const int tok = __builtin_amdgcn_readlane(tokv, row);
+            const int kc = 64 * i + lane;
+            if (kc < spr)
                 __builtin_amdgcn_global_load_lds(
                     (const MOE_GLOBAL void *)(x + (size_t)tok * K + 8 * (kc < cpr ? kc : 0)),
-                    (MOE_LDS void *)(xb + 16 * base), 16, 0, 0);
-            kc += 64 * kWaves;
-            while (kc >= spr) {
-                kc -= spr;
-                ++m;
+                    (MOE_LDS void *)(xb + 16 * (row * spr + 64 * i)), 16, 0, 0);
+            i += kWaves;
+            while (i >= nit) {
+                i -= nit;
+                ++row;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -278,26 +288,45 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
         const int tm = (int)threadIdx.x >> lgt, tj = (int)threadIdx.x & ((1 << lgt) - 1);
         const bool rin = tm < pr;
         uint16_t *xr = xs + (rin ? tm : 0) * ldx;
+        // kIlp chunks per iteration, their LDS reads issued together (a
+        // chunk past the row's end reads the iteration's first again).
+        constexpr int kIlp = 8;
+        const int cst = 1 << lgt;
         u16x2_t mx = {0, 0};
         if (rin)
-            for (int c = tj; c < cpr; c += 1 << lgt)
-                mx = __builtin_elementwise_max(mx, absmax8_bf16(*reinterpret_cast<const uint4 *>(xr + 8 * c)));
+            for (int c = tj; c < cpr; c += kIlp * cst) {
+                uint4 v[kIlp];
+#pragma unroll
+                for (int u = 0; u < kIlp; ++u) {
+                    const int cc = c + u * cst;
+                    v[u] = *reinterpret_cast<const uint4 *>(xr + 8 * (cc < cpr ? cc : c));
+                }
+#pragma unroll
+                for (int u = 0; u < kIlp; ++u) mx = __builtin_elementwise_max(mx, absmax8_bf16(v[u]));
+            }
         // float bits of the largest magnitude
         row_group_max(rmax, tm, rin, (uint32_t)(mx.x > mx.y ? mx.x : mx.y) << 16, lgt);
         moe::lds_barrier();  // maxima complete
-        if (rin) {  // bf16 -> scaled fp16 in place
+        if (rin) {  // bf16 -> scaled fp16 in place, kIlp chunks per iteration
             const float f = exp2i(-row_exp(rmax[tm]));
-            for (int c = tj; c < cpr; c += 1 << lgt) {
-                uint4 *p = reinterpret_cast<uint4 *>(xr + 8 * c);
-                const uint4 v = *p;
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-                f16x8_t h;
+            for (int c = tj; c < cpr; c += kIlp * cst) {
+                uint4 v[kIlp];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h[2 * i] = (_Float16)(bf16_lo(u[i]) * f);
-                    h[2 * i + 1] = (_Float16)(bf16_hi(u[i]) * f);
+                for (int u = 0; u < kIlp; ++u) {
+                    const int cc = c + u * cst;
+                    v[u] = *reinterpret_cast<const uint4 *>(xr + 8 * (cc < cpr ? cc : c));
                 }
-                *reinterpret_cast<f16x8_t *>(p) = h;
+#pragma unroll
+                for (int u = 0; u < kIlp; ++u) {
+                    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    f16x8_t h;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        h[2 * j] = (_Float16)(bf16_lo(w4[j]) * f);
+                        h[2 * j + 1] = (_Float16)(bf16_hi(w4[j]) * f);
+                    }
+                    if (c + u * cst < cpr) *reinterpret_cast<f16x8_t *>(xr + 8 * (c + u * cst)) = h;
+                }
             }
         }
         moe::lds_barrier();
@@ -336,28 +365,46 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
             for (int i = 0; i < SB; ++i)
                 if (valid(i)) put_f16x8(dst + 8 * (tj + (i << lgt)), f0[i], f1[i], f);
         } else {
-            // Several batches: maxima first, then the rows read again (L2 hits).
-            auto batch = [&](int b, auto first) {
-                f32x4_t f0[SB], f1[SB];
+            // Several batches: maxima first, then the rows read again (L2
+            // hits).  Two register sets: each batch's loads go out before the
+            // previous batch is used, so the batches' round trips overlap
+            // (the loads past the last batch re-read valid chunks, unused).
+            // The weight ring goes out after the conversion's first two
+            // batches: loads complete in issue order, so a wait for an h
+            // batch issued before the ring does not wait for weights.
+            f32x4_t a0[SB], a1[SB], b0[SB], b1[SB];
+            auto ldb = [&](int b, f32x4_t *f0, f32x4_t *f1) {
 #pragma unroll
                 for (int i = 0; i < SB; ++i) ld(b + i, f0[i], f1[i]);
-                if constexpr (decltype(first)::value) mid();
+            };
+            auto mxb = [&](int b, const f32x4_t *f0, const f32x4_t *f1) {
 #pragma unroll
                 for (int i = 0; i < SB; ++i)
                     if (valid(b + i)) mx = max(mx, __float_as_uint(absmax8f(f0[i], f1[i])));
             };
-            batch(0, std::true_type{});
-            for (int b = SB; b < nct; b += SB) batch(b, std::false_type{});
-            row_group_max(rmax, tm, rin, mx, lgt);
-            __syncthreads();  // maxima complete
-            const float f = exp2i(-row_exp(rmax[rin ? tm : 0]));
-            for (int b = 0; b < nct; b += SB) {
-                f32x4_t f0[SB], f1[SB];
-#pragma unroll
-                for (int i = 0; i < SB; ++i) ld(b + i, f0[i], f1[i]);
+            auto cvb = [&](int b, const f32x4_t *f0, const f32x4_t *f1, float f) {
 #pragma unroll
                 for (int i = 0; i < SB; ++i)
                     if (valid(b + i)) put_f16x8(dst + 8 * (tj + ((b + i) << lgt)), f0[i], f1[i], f);
+            };
+            ldb(0, a0, a1);
+            for (int b = 0; b < nct; b += 2 * SB) {
+                ldb(b + SB, b0, b1);
+                mxb(b, a0, a1);
+                ldb(b + 2 * SB, a0, a1);
+                mxb(b + SB, b0, b1);
+            }
+            row_group_max(rmax, tm, rin, mx, lgt);
+            __syncthreads();  // maxima complete
+            const float f = exp2i(-row_exp(rmax[rin ? tm : 0]));
+            ldb(0, a0, a1);
+            ldb(SB, b0, b1);
+            mid();
+            for (int b = 0; b < nct; b += 2 * SB) {
+                cvb(b, a0, a1, f);
+                ldb(b + 2 * SB, a0, a1);
+                cvb(b + SB, b0, b1, f);
+                ldb(b + 3 * SB, b0, b1);
             }
         }
         __syncthreads();
@@ -946,6 +993,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     }
 }
 
+// floor(n / d) for 0 <= n < 2^52 and d > 0, through one fp64 division (its
+// quotient is within one of the true one) and an exact integer correction;
+// a 64-bit integer division is a long instruction sequence on this hardware.
+__device__ __forceinline__ int64_t div_floor(int64_t n, int64_t d) {
+    int64_t q = (int64_t)((double)n / (double)d);
+    q = q * d > n ? q - 1 : q;
+    q = (q + 1) * d <= n ? q + 1 : q;
+    return q;
+}
+
 // Relative cost of one unit of a pass with r routed rows, for the share
 // walk (token groups of 4 share each decoded weight; the weight stream
 // itself costs the same).  On the 64-token launch the flatter model below
@@ -1147,7 +1204,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         // per pass, measured 8% slower this way.)  The points are placed on
         // the unit_cost_one prefix.
         const int total1 = pre1[n];
-        const int64_t pt = ((int64_t)(2 * bx + 1) * total1) / (2 * (int64_t)g);
+        const int64_t pt = div_floor((int64_t)(2 * bx + 1) * total1, 2 * (int64_t)g);
         const int sl = find_slot(pre1, n, (int)pt);
         const SlotInfo in = si[sl];
         const int pr = a.pass_rows;
@@ -1161,18 +1218,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         // blocks whose points lie in [ps, ps + pc): (2b + 1) total1 in [2 g ps, 2 g (ps + pc))
         auto first_at = [&](int64_t c) -> int64_t {
             const int64_t v = 2 * (int64_t)g * c - total1;
-            return v <= 0 ? 0 : (v + 2 * (int64_t)total1 - 1) / (2 * (int64_t)total1);
+            return v <= 0 ? 0 : div_floor(v + 2 * (int64_t)total1 - 1, 2 * (int64_t)total1);
         };
         const int b_lo = (int)first_at(ps), nb = (int)(first_at(ps + pc) - b_lo);
         const int i = bx - b_lo;
-        const int u0 = (int)((int64_t)i * a.units / nb), u1 = (int)((int64_t)(i + 1) * a.units / nb);
+        const int u0 = (int)div_floor((int64_t)i * a.units, nb), u1 = (int)div_floor((int64_t)(i + 1) * a.units, nb);
         __syncthreads();  // the set-up's readers of LDS are done
         if (u1 > u0)
             do_pass_rows<GATED, SORT, true>(a, in.e, in.lo, in.lo + in.rows, p, u0, u1 - u0, nt_ok, lds, tokl);
         return;
     }
-    const int c0 = (int)((int64_t)total * bx / g);
-    const int c1 = (int)((int64_t)total * (bx + 1) / g);
+    const int c0 = (int)div_floor((int64_t)total * bx, g);
+    const int c1 = (int)div_floor((int64_t)total * (bx + 1), g);
     Cursor k = locate(a, pre, si, n, c0);
     const Cursor end = locate(a, pre, si, n, c1);
     // The share's first slots move to registers (lane l, entry j: slot

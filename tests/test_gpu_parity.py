@@ -309,6 +309,16 @@ def test_many_experts_and_passes(routing, kmajor):
     _full_check(Case(17, shape), f"wide {routing} {kmajor}")
 
 
+def test_layer_many_sparse_experts():
+    """256 routed pairs over about 225 of 1024 experts, H = 2048: the
+    persistent gate+up (sort inside) walks shares that cross expert
+    boundaries, and the down projection's grid holds about 225 live expert
+    rows; the whole layer against the oracle."""
+    say("layer over many sparse experts")
+    shape = synth.MoeShape("sparse_e1024", 32, 2048, 512, 1024, 8, "uniform", False)
+    _full_check(Case(28, shape), "many sparse experts")
+
+
 def test_kmajor_few_experts_many_rows():
     """4 experts, 700 tokens, top-2: about 350 rows per expert, so every
     expert is split into several balanced row tiles in both projections."""
