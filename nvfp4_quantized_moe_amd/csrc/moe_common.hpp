@@ -189,15 +189,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // (on return the exclusive offsets, offs[E] = valid pairs), cntw[4 * E],
 // act[E] (on return the active experts ascending), stok[P] (on return the
 // token of each sorted position below offs[E]).  Returns the active count.
-// With `out` set, also writes every output of moe_nvfp4_sort to memory.
-// Ends with a barrier.
+// With `wr` set, also writes every output of moe_nvfp4_sort to memory.  (The
+// outputs come by value with a flag, not as a pointer that may be null: a
+// select between the address of a local and null kept the struct on the
+// stack, a private-memory write by every lane of every block.)  Ends with a
+// barrier.
 struct SortOutputs {
     int32_t *offsets, *sorted_tok, *pair_pos, *active, *active_count;
     uint32_t *err_flag;
 };
 constexpr int kBlockSortPairs = 256;
 __device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, int E, int *offs, int *cntw,
-                                              int *act, int *stok, const SortOutputs *out) {
+                                              int *act, int *stok, const SortOutputs out, const bool wr) {
     __shared__ int wsum[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = tid < P ? ids[tid] : -1;
@@ -207,8 +210,8 @@ __device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, 
 #pragma unroll
         for (int w = 0; w < 4; ++w) cntw[w * E + i] = 0;
     }
-    if (out && __ballot(tid < P && !valid) != 0ull && lane == 0)
-        atomicOr(out->err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
+    if (wr && __ballot(tid < P && !valid) != 0ull && lane == 0)
+        atomicOr(out.err_flag, MOE_NVFP4_FLAG_BAD_EXPERT_ID);
     __syncthreads();
     if (valid) {
         atomicAdd(&offs[e], 1);
@@ -258,10 +261,10 @@ __device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, 
         if (ex < E) {
             offs[ex] = off;
             if (c[i] > 0) act[aidx] = ex;
-            if (out) {
-                out->offsets[ex] = off;
-                if (c[i] > 0) out->active[aidx] = ex;
-                if (ex >= t1) out->active[ex] = -1;
+            if (wr) {
+                out.offsets[ex] = off;
+                if (c[i] > 0) out.active[aidx] = ex;
+                if (ex >= t1) out.active[ex] = -1;
             }
             aidx += c[i] > 0 ? 1 : 0;
         }
@@ -269,9 +272,9 @@ __device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, 
     }
     if (tid == 0) {
         offs[E] = t0;
-        if (out) {
-            out->offsets[E] = t0;
-            *out->active_count = t1;
+        if (wr) {
+            out.offsets[E] = t0;
+            *out.active_count = t1;
         }
     }
     __syncthreads();
@@ -284,14 +287,14 @@ __device__ __forceinline__ int block_sort_256(const int32_t *ids, int P, int k, 
         if (tid < P) {
             const int pos = valid ? offs[e] + rank : -1;
             if (valid) stok[pos] = tid / k;
-            if (out) {
-                out->pair_pos[tid] = pos;
-                if (valid) out->sorted_tok[pos] = tid / k;
+            if (wr) {
+                out.pair_pos[tid] = pos;
+                if (valid) out.sorted_tok[pos] = tid / k;
             }
         }
     }
-    if (out)
-        for (int q = t0 + tid; q < P; q += 256) out->sorted_tok[q] = -1;
+    if (wr)
+        for (int q = t0 + tid; q < P; q += 256) out.sorted_tok[q] = -1;
     __syncthreads();
     return t1;
 }

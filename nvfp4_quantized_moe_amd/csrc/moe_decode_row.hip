@@ -412,10 +412,10 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
 }
 
 // One pass: rows [row0, row0 + pr) of the expert against units
-// [u_first, u_first + nu) of its weights.
+// u_first + us i, i in [0, nu), of its weights (us = 1: a contiguous range).
 // A pass of up to 4 rows in the (row, quarter) layout.
 template <bool GATED, int D, bool TOK_LDS, bool NT>  // TOK_LDS: tokens from the fused sort's LDS table tokl
-__device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu,
+__device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int u_first, int nu, int us,
                                          const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
                                          const uint8_t *sB, float s2A, float s2B, uint8_t *lds,
                                          const int *tokl) {
@@ -471,10 +471,10 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
             const int want = 32 * l + 16 * hh;
             const int got = min(want, sbytes - 16);
             ssh[d / kGroup] = (want - got) >> 2;
-            sv[d / kGroup] = moe::gload<u32x4_t>(sbase + (size_t)(u_first + u) * sustride + got);
+            sv[d / kGroup] = moe::gload<u32x4_t>(sbase + (size_t)(u_first + us * u) * sustride + got);
         }
         const bool real = lu < nu;  // past the end: the last real step again
-        const int unit = u_first + (real ? lu : nu - 1);
+        const int unit = u_first + us * (real ? lu : nu - 1);
         const int off = min(kSegBytes * (real ? li : nseg - 1) + choff, rowbytes - 16);
         w0[d] = wload<NT>(wb0 + (size_t)unit * ustride + off);
         w1[d] = wload<NT>(wb1 + (size_t)unit * ustride + off);
@@ -569,7 +569,7 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
             acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[ks], b1[ks], acc1, 0, 0, 0);
         }
         if (cu < nu && ci == nseg - 1) {  // uniform: this unit is complete
-            const int unit = u_first + cu;
+            const int unit = u_first + us * cu;
             // Lane (n, q) holds rows 4q..4q+3 of column n; the kept block is
             // row 4q + (n & 3), i.e. token q.  Sum the quarters of a quad.
             const float g0 = moe::group_sum<4>(pick(acc0, c)) * oscale;
@@ -624,7 +624,7 @@ __device__ __forceinline__ void run_pass(const DecArgs &a, int row0, int pr, int
 //     step: two windows) into the wave's 1 KiB LDS area; a step reads its
 //     two bytes per window per lane from there.
 template <bool GATED, int D, bool TOK_LDS>
-__device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int pr, int u_first, int nu,
+__device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int pr, int u_first, int nu, int us,
                                                const uint8_t *pA, const uint8_t *sA, const uint8_t *pB,
                                                const uint8_t *sB, float s2A, float s2B, uint8_t *lds,
                                                const int *tokl) {
@@ -635,12 +635,13 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
     const int nstep = (nwin + 1) >> 1;      // two windows per step
     const int lane = threadIdx.x & 63, w = moe::wave_id();
     const int n = lane & 15, q = lane >> 4;
-    const int i_first = 2 * u_first, nit = 2 * nu;  // items of the block
-    const int niw = nit > w ? (nit - w + 3) >> 2 : 0;  // items of this wave: i_first + w + 4 j
+    const int nit = 2 * nu;  // items of the block: item b is half b & 1 of unit u_first + us (b >> 1)
+    auto item_of = [&](int b) { return 2 * (u_first + us * (b >> 1)) + (b & 1); };
+    const int niw = nit > w ? (nit - w + 3) >> 2 : 0;  // items of this wave: item_of(w + 4 j)
     const int total = niw * nstep;
     // Item read past the end of this wave's list (a wave with none reads the
     // block's first item): the addresses stay inside the expert's weights.
-    const int last_item = niw > 0 ? i_first + w + 4 * (niw - 1) : i_first;
+    const int last_item = item_of(niw > 0 ? w + 4 * (niw - 1) : 0);
 
     uint8_t *sc_lds = lds + w * kScaleLds;
     uint32_t *rmax = reinterpret_cast<uint32_t *>(lds + kRmaxOff);
@@ -672,7 +673,7 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
                 j = wrap ? j + 1 : j;
             }
             const bool real = j < niw;
-            const int item = real ? i_first + w + 4 * j : last_item;
+            const int item = real ? item_of(w + 4 * j) : last_item;
             l = real ? l : nstep - 1;
             const int want = 16 * l;
             const int got = min(want, sbytes - 16);
@@ -680,7 +681,7 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
             sv[d / kGroup] = moe::gload<u32x4_t>(sb + (size_t)item * sistride + got);
         }
         const bool real = lj < niw;  // past the end: the last real step again
-        const int item = real ? i_first + w + 4 * lj : last_item;
+        const int item = real ? item_of(w + 4 * lj) : last_item;
         const int st = real ? ls : nstep - 1;
         const uint8_t *rb = wb + (size_t)item * istride;
         w0[d] = moe::gload<u32x4_t>(rb + min(128 * st + 16 * q, rowbytes - 16));
@@ -758,7 +759,7 @@ __device__ __forceinline__ void run_pass_dense(const DecArgs &a, int row0, int p
             }
         }
         if (cj < niw && cs == nstep - 1) {  // uniform: this item is complete
-            const int item = i_first + w + 4 * cj;
+            const int item = item_of(w + 4 * cj);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = 4 * q + v;  // C row (pass row) of acc[v]; column n
@@ -845,9 +846,11 @@ __device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
 }
 
 // One pass of expert e, whose rows are the sorted positions [lo, hi).
+// Units u_first + us i, i in [0, nu).
 template <bool GATED, bool TOK_LDS, bool NT_OK>  // NT_OK: built with the nontemporal variant
 __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, int hi, int pass, int u_first,
-                                             int nu, bool nt_ok, uint8_t *lds, const int *tokl = nullptr) {
+                                             int nu, bool nt_ok, uint8_t *lds, const int *tokl = nullptr,
+                                             int us = 1) {
     // Every table entry of expert e is read at once (e < E, so each read is
     // in bounds): one round of dependent loads, not one per table.
     const uint8_t *pA = a.pa[e];
@@ -864,10 +867,10 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
     const int pr = min(a.pass_rows, rows - m0);
     constexpr int ucols = GATED ? 16 : 32;
     if (pA == nullptr || pB == nullptr || sA == nullptr || sB == nullptr) {  // absent expert: its rows are zero
-        const int ncols = nu * ucols, n0 = u_first * ucols;
+        const int ncols = nu * ucols;
         for (int i = threadIdx.x; i < pr * ncols; i += kThreads) {
-            const int m = i / ncols;
-            a.out[(size_t)(lo + m0 + m) * a.N + n0 + (i - m * ncols)] = 0.f;
+            const int m = i / ncols, c = i - m * ncols, k = c / ucols;
+            a.out[(size_t)(lo + m0 + m) * a.N + (u_first + us * k) * ucols + (c - k * ucols)] = 0.f;
         }
         return;
     }
@@ -876,11 +879,11 @@ __device__ __forceinline__ void do_pass_rows(const DecArgs &a, int e, int lo, in
     // Nontemporal weight loads: a large launch, and an expert read by this
     // pass alone.
     if (pr > 4)
-        run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
+        run_pass_dense<GATED, kDepth, TOK_LDS>(a, lo + m0, pr, u_first, nu, us, pA, sA, pB, sB, s2A, s2B, lds, tokl);
     else if (NT_OK && nt_ok && rows <= a.pass_rows)
-        run_pass<GATED, kDepth, TOK_LDS, NT_OK>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
+        run_pass<GATED, kDepth, TOK_LDS, NT_OK>(a, lo + m0, pr, u_first, nu, us, pA, sA, pB, sB, s2A, s2B, lds, tokl);
     else
-        run_pass<GATED, kDepth, TOK_LDS, false>(a, lo + m0, pr, u_first, nu, pA, sA, pB, sB, s2A, s2B, lds, tokl);
+        run_pass<GATED, kDepth, TOK_LDS, false>(a, lo + m0, pr, u_first, nu, us, pA, sA, pB, sB, s2A, s2B, lds, tokl);
 }
 
 template <bool GATED, bool NT_OK>
@@ -965,10 +968,10 @@ template <bool GATED, bool SORT>  // SORT: gate+up with the routing sort fused i
 __global__ __launch_bounds__(kThreads) void k_decode_row(DecArgs a) {
     extern __shared__ uint4 lds4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
-    const int u_first = blockIdx.x * a.G;
+    const int bx = blockIdx.x, y = blockIdx.y;
+    const int u_first = bx * a.G;
     const int nu = min(a.G, a.units - u_first);
     if (nu <= 0) return;
-    const int y = blockIdx.y;
     if constexpr (GATED && SORT) {  // extra == 0: one pass per expert
         const int3 r = fused_sort(a, reinterpret_cast<SortLds *>(lds + kPreOff), y);
         if (r.x < 0) return;  // past the active count
@@ -1167,8 +1170,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         si = reinterpret_cast<SlotInfo *>(act + a.E);
         pre1 = reinterpret_cast<int *>(si + a.cap);
         const moe::SortOutputs out{a.sort_offsets, a.sort_tok, a.sort_pos, a.sort_active, a.sort_count, a.err_flag};
-        n = moe::block_sort_256(a.topk_ids, a.P, a.topk, a.E, offs, cntw, act, stok,
-                                blockIdx.x == 0 ? &out : nullptr);
+        n = moe::block_sort_256(a.topk_ids, a.P, a.topk, a.E, offs, cntw, act, stok, out, blockIdx.x == 0);
         tokl = stok;
         cost_prefix(a, n, pre, pre1, si, pass_min, [&](int sl) {
             const int e = sl < n ? act[sl] : -1;
@@ -1222,8 +1224,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_row_persist(DecArgs a) {
         };
         const int b_lo = (int)first_at(ps), nb = (int)(first_at(ps + pc) - b_lo);
         const int i = bx - b_lo;
-        const int u0 = (int)div_floor((int64_t)i * a.units, nb), u1 = (int)div_floor((int64_t)(i + 1) * a.units, nb);
         __syncthreads();  // the set-up's readers of LDS are done
+        if (in.rows > pr) {
+            // An expert with several passes: block i of a pass takes units
+            // i, i + nb, i + 2 nb, ...  Each pass has blocks in proportion to
+            // its cost, so every pass of the expert sweeps the units at about
+            // the same pace, and its blocks sit next to each other in bx (one
+            // XCD): a pass reading a unit after another pass mostly finds it
+            // in L2, where contiguous ranges of different lengths per pass
+            // read each unit at unrelated times.
+            const int nu = i < a.units ? (a.units - i + nb - 1) / nb : 0;
+            if (nu > 0)
+                do_pass_rows<GATED, SORT, true>(a, in.e, in.lo, in.lo + in.rows, p, i, nu, nt_ok, lds, tokl, nb);
+            return;
+        }
+        const int u0 = (int)div_floor((int64_t)i * a.units, nb), u1 = (int)div_floor((int64_t)(i + 1) * a.units, nb);
         if (u1 > u0)
             do_pass_rows<GATED, SORT, true>(a, in.e, in.lo, in.lo + in.rows, p, u0, u1 - u0, nt_ok, lds, tokl);
         return;

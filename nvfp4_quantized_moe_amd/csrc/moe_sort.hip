@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_sort_small(
     __shared__ int act[MOE_NVFP4_MAX_EXPERTS];
     __shared__ int stok[kSmallPairs];
     const moe::SortOutputs out{offsets, sorted_tok, pair_pos, active, active_count, err_flag};
-    moe::block_sort_256(ids, P, k, E, offs, cntw, act, stok, &out);
+    moe::block_sort_256(ids, P, k, E, offs, cntw, act, stok, out, true);
 }
 
 }  // namespace
