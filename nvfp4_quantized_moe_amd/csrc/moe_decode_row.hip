@@ -365,13 +365,24 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
             for (int i = 0; i < SB; ++i)
                 if (valid(i)) put_f16x8(dst + 8 * (tj + (i << lgt)), f0[i], f1[i], f);
         } else {
-            // Several batches: maxima first, then the rows read again (L2
-            // hits).  Two register sets: each batch's loads go out before the
+            // Several batches, read once.  Each row's scale comes from the
+            // largest magnitude of its threads' first batch (a lower bound on
+            // the row's), doubled: the estimate lands in [2^13, 2^14), so any
+            // element up to 4x it still converts to a finite fp16 number.
+            // Scaling by a power of two leaves the fp16 rounding of a normal
+            // number unchanged, so the staged values (and every sum over
+            // them) are those of the exact row maximum's scale, up to that
+            // power of two, which the epilogue undoes from rmax.  Every
+            // thread tracks the largest magnitude it converts; a row with an
+            // element at or past the fp16 limit at this scale (or not
+            // finite), or whose estimate is zero, makes the whole block stage
+            // again from exact maxima: the rows read twice, maxima first.
+            // Two register sets: each batch's loads go out before the
             // previous batch is used, so the batches' round trips overlap
             // (the loads past the last batch re-read valid chunks, unused).
-            // The weight ring goes out after the conversion's first two
-            // batches: loads complete in issue order, so a wait for an h
-            // batch issued before the ring does not wait for weights.
+            // The weight ring goes out once the estimates are known: loads
+            // complete in issue order, so the wait for the first batch does
+            // not wait for weights.
             f32x4_t a0[SB], a1[SB], b0[SB], b1[SB];
             auto ldb = [&](int b, f32x4_t *f0, f32x4_t *f1) {
 #pragma unroll
@@ -387,24 +398,59 @@ __device__ __forceinline__ void stage(const DecArgs &a, int row0, int pr, const 
                 for (int i = 0; i < SB; ++i)
                     if (valid(b + i)) put_f16x8(dst + 8 * (tj + ((b + i) << lgt)), f0[i], f1[i], f);
             };
-            ldb(0, a0, a1);
-            for (int b = 0; b < nct; b += 2 * SB) {
-                ldb(b + SB, b0, b1);
-                mxb(b, a0, a1);
-                ldb(b + 2 * SB, a0, a1);
-                mxb(b + SB, b0, b1);
-            }
-            row_group_max(rmax, tm, rin, mx, lgt);
-            __syncthreads();  // maxima complete
-            const float f = exp2i(-row_exp(rmax[rin ? tm : 0]));
+            // (The gathered staging of the fused down+blend launch keeps the
+            // two reads: its few rows mostly take the one-batch path, and the
+            // single-read code would cost it a wave per SIMD.)
+            bool twice = GATHER;
+            if constexpr (!GATHER) {
             ldb(0, a0, a1);
             ldb(SB, b0, b1);
+            mxb(0, a0, a1);
+            row_group_max(rmax, tm, rin, mx, lgt);
+            __syncthreads();  // first-batch maxima complete
+            const uint32_t est = rmax[rin ? tm : 0];
+            __syncthreads();  // every estimate is read before the rows' scales replace them
+            const uint32_t sc = est + (1u << 23);  // the estimate doubled (non-finite: row_exp gives 0)
+            if (rin && tj == 0) rmax[tm] = sc;
+            const int es = row_exp(sc);
+            const float f = exp2i(-es);
+            const uint32_t lim = __float_as_uint(65504.f * exp2i(es));  // largest magnitude that stays finite
             mid();
             for (int b = 0; b < nct; b += 2 * SB) {
+                if (b > 0) mxb(b, a0, a1);  // the first batch's maximum is in mx already
                 cvb(b, a0, a1, f);
                 ldb(b + 2 * SB, a0, a1);
+                mxb(b + SB, b0, b1);
                 cvb(b + SB, b0, b1, f);
                 ldb(b + 3 * SB, b0, b1);
+            }
+            twice = __syncthreads_or(rin && (est == 0u || mx >= lim));
+            if (twice) {
+                if ((int)threadIdx.x < pr) rmax[threadIdx.x] = 0u;
+                __syncthreads();
+                mx = 0u;
+            }
+            }
+            if (twice) {
+                ldb(0, a0, a1);
+                for (int b = 0; b < nct; b += 2 * SB) {
+                    ldb(b + SB, b0, b1);
+                    mxb(b, a0, a1);
+                    ldb(b + 2 * SB, a0, a1);
+                    mxb(b + SB, b0, b1);
+                }
+                row_group_max(rmax, tm, rin, mx, lgt);
+                __syncthreads();  // exact maxima complete
+                const float fx = exp2i(-row_exp(rmax[rin ? tm : 0]));
+                ldb(0, a0, a1);
+                ldb(SB, b0, b1);
+                if constexpr (GATHER) mid();  // (single read: the ring is out already)
+                for (int b = 0; b < nct; b += 2 * SB) {
+                    cvb(b, a0, a1, fx);
+                    ldb(b + 2 * SB, a0, a1);
+                    cvb(b + SB, b0, b1, fx);
+                    ldb(b + 3 * SB, b0, b1);
+                }
             }
         }
         __syncthreads();

@@ -716,3 +716,53 @@ def test_kmajor_down_row_exponents(fmt):
                 assert not y[p].any(), p
                 continue
             parity.assert_parity_relative(y[p], y_ref[p - lo], f"{fmt} y row {p}")
+
+
+# ---------------------------------------------------------------- row-major down: row scales of h
+def test_rowmajor_down_row_scales():
+    """The row-major down projection stages a pass's h rows as fp16 with one
+    power of two per row.  With rows read in several batches it reads them
+    once, the scale set by the first batch's largest magnitude (with a
+    factor 4 of headroom); a row whose later elements pass the fp16 limit at
+    that scale, or whose first batch is all zero, makes the block stage again
+    from exact maxima.  I = 1856 over two experts (passes of 16 and 8 rows,
+    so every pass takes several batches, the first covering at most the
+    first 1024 elements).  Crafted rows: the first 32 elements 2^-12 of the
+    rest, zeros up to k = 200, all zeros, scaled by 2^60 and 2^-60, a tail
+    from k = 1100 grown by 2^20 (overflow at the estimated scale), zeros up
+    to k = 1100 (an all-zero first batch), and plain rows.  Each y row is
+    compared with the oracle at its own magnitude; zero rows give zero."""
+    say("row-major down row scales")
+    shape = synth.MoeShape("down_rows_rm", 40, 512, 1856, 2, 2, "uniform", False)
+    case = Case(28, shape)
+    case.run()  # the sort outputs the down launch indexes with
+    L, P, I = case.layer, shape.P, shape.I
+    h = np.random.default_rng(28).standard_normal((P, I))
+    h[0::8, :32] *= 2.0 ** -12
+    h[1::8, :200] = 0.0
+    h[2::8, :] = 0.0
+    h[3::8] *= 2.0 ** 60
+    h[4::8] *= 2.0 ** -60
+    h[5::8, 1100:] *= 2.0 ** 20
+    h[6::8, :1100] = 0.0
+    h32 = h.astype(np.float32)
+    L.h.copy_(torch.from_numpy(h32).cuda())
+    L.y.fill_(7.0)
+    moe.moe_nvfp4_down(L.h, shape.T, shape.k, shape.E, shape.H, shape.I, L.down, L.expert_offsets,
+                       L.active_experts, L.active_count, L.y)
+    torch.cuda.synchronize()
+    y = _h2f(L.y)
+    offs = L.expert_offsets.cpu().numpy()
+    say("rows per expert", np.diff(offs).tolist())
+    wf = case.weight_fn()
+    for e in range(shape.E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi == lo:
+            continue
+        Wd = oracle.expert_weights(wf, e, shape.H, shape.I, False)[2]
+        y_ref = oracle.down_rows(h32[lo:hi].astype(np.float64), Wd)
+        for p in range(lo, hi):
+            if not h32[p].any():
+                assert not y[p].any(), p
+                continue
+            parity.assert_parity_relative(y[p], y_ref[p - lo], f"row-major y row {p}")
