@@ -880,15 +880,23 @@ __device__ __forceinline__ void pass_prefix(const DecArgs &a, int n, int *pre) {
     __syncthreads();
 }
 
-// Last slot s < n with pre[s] <= g (pre non-decreasing, pre[0] = 0 <= g).
+// Last slot s < n with pre[s] <= g (pre non-decreasing, pre[0] = 0 <= g),
+// found by the lanes of the calling wave together: lane l tests slot
+// base + l, and the qualifying slots form a prefix, so the answer is the
+// highest qualifying lane of the first chunk of 64 slots that does not
+// qualify whole (one LDS read per lane per chunk, not a chain of dependent
+// reads).  Wave-uniform.
 __device__ __forceinline__ int find_slot(const int *pre, int n, int g) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= g) lo = mid;
-        else hi = mid - 1;
+    const int lane = threadIdx.x & 63;
+    int best = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int s = base + lane;
+        const unsigned long long m = __ballot(s < n && pre[s] <= g);
+        if (m == 0ull) break;
+        best = base + 63 - __clzll((long long)m);
+        if (m != ~0ull) break;
     }
-    return lo;
+    return best;
 }
 
 // One pass of expert e, whose rows are the sorted positions [lo, hi).
