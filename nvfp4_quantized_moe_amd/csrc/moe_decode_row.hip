@@ -1014,7 +1014,8 @@ __device__ __forceinline__ int3 fused_sort(const DecArgs &a, SortLds *sl, int sl
     return r;
 }
 
-// Block (x, y): units [x G, x G + G) of
+// Block (x, y) of a grid of nx = ceil(units / G) columns: units x, x + nx,
+// x + 2 nx, ... (at most G; with the fused sort, units [x G, x G + G)) of
 //   y >= extra: the first pass (rows 0 .. pass_rows) of active slot y - extra;
 //   y <  extra: further passes number y, y + extra, ... in slot order, so an
 //               expert with many routed rows is spread over many blocks of
