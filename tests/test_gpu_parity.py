@@ -222,6 +222,28 @@ def test_null_expert_contributes_zero(kmajor):
     assert not _h2f(case.layer.h)[lo:hi].any() and not _h2f(case.layer.y)[lo:hi].any()
 
 
+def test_null_experts_in_the_32_token_launches():
+    """The 32-token workload (persistent gate+up with the sort inside, one
+    pass per block over strided unit shares; down as one block per strided
+    unit group) with two NULL experts: the busiest one, whose rows take
+    several passes, and one with a single routed row.  Their h and y rows
+    are zero (written for every strided unit), and the whole layer matches
+    the oracle, in which a NULL expert contributes nothing."""
+    say("null experts at 32 tokens")
+    shape = synth.config(3)
+    ids, _ = synth.gen_routing(3, shape)
+    cnt = np.bincount(ids.reshape(-1), minlength=shape.E)
+    e_busy = int(np.argmax(cnt))
+    e_one = int(np.nonzero(cnt == 1)[0][0])
+    say("busy expert", e_busy, "rows", int(cnt[e_busy]), "one-row expert", e_one)
+    case = Case(3, nulls=(e_busy, e_one))
+    ref = _full_check(case, "null experts t32")
+    h, y = _h2f(case.layer.h), _h2f(case.layer.y)
+    for e in (e_busy, e_one):
+        lo, hi = ref["expert_offsets"][e], ref["expert_offsets"][e + 1]
+        assert hi > lo and not h[lo:hi].any() and not y[lo:hi].any(), e
+
+
 def test_invalid_ids_flagged_and_skipped():
     say("invalid ids")
     shape = synth.MoeShape("bad", 8, 256, 512, 4, 2, "uniform", False)
